@@ -1,0 +1,115 @@
+// qmm.cpp — the C ABI: argument validation, then dispatch to the kernels.
+// Every check runs before anything is enqueued, so an error return leaves
+// every output untouched.  Nothing here allocates, copies or synchronizes.
+#include <limits.h>
+#include <stdint.h>
+
+#include "qmm_internal.h"
+
+using namespace qmm;
+
+namespace {
+
+constexpr int64_t kMaxK = 65536;  // activation rows must fit the GEMV's LDS staging
+
+bool is_type(int t) { return t >= QMM_Q4_0 && t <= QMM_Q8_K; }
+bool is_weight(int t) { return t == QMM_Q4_0 || t == QMM_Q8_0 || t == QMM_Q4_K || t == QMM_Q6_K; }
+
+int check_ptr(const void* p) {
+    if (!p) return QMM_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return QMM_ERR_ALIGN;
+    return QMM_OK;
+}
+
+// rows x K values of type t: positive sizes, whole blocks, and byte counts
+// (blocks and fp32) that fit comfortably in int64.
+int check_dims(int t, int64_t rows, int64_t K) {
+    if (rows <= 0 || K <= 0) return QMM_ERR_SHAPE;
+    const int B = block_size(t);
+    if (K % B) return QMM_ERR_SHAPE;
+    const int64_t lim = INT64_MAX / 8;
+    if (K > lim / 4 || rows > lim / (K * 4)) return QMM_ERR_SHAPE;  // rows*K*4 fp32 bytes
+    return QMM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int qmm_block_size(int type) { return is_type(type) ? block_size(type) : 0; }
+
+size_t qmm_block_bytes(int type) { return is_type(type) ? (size_t)block_bytes(type) : 0; }
+
+size_t qmm_row_bytes(int type, int64_t K) {
+    if (!is_type(type) || K <= 0 || K % block_size(type)) return 0;
+    if (K > INT64_MAX / 8 / 4) return 0;
+    return (size_t)(K / block_size(type)) * (size_t)block_bytes(type);
+}
+
+int qmm_vec_dot_type(int wtype) {
+    if (!is_type(wtype)) return QMM_ERR_TYPE;
+    if (wtype == QMM_Q4_0 || wtype == QMM_Q8_0) return QMM_Q8_0;
+    if (wtype == QMM_Q4_K || wtype == QMM_Q6_K) return QMM_Q8_K;
+    return QMM_ERR_UNSUPPORTED;
+}
+
+int qmm_quantize(int dst, const float* x, void* out, int64_t rows, int64_t K, void* stream) {
+    if (!is_type(dst)) return QMM_ERR_TYPE;
+    if (dst != QMM_Q8_0 && dst != QMM_Q8_K && dst != QMM_Q4_0) return QMM_ERR_UNSUPPORTED;
+    int rc;
+    if ((rc = check_ptr(x)) || (rc = check_ptr(out))) return rc;
+    if ((rc = check_dims(dst, rows, K))) return rc;
+    return hip_status(launch_quantize(dst, x, out, rows, K, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_quantize_act(int dst, const float* x, void* xq, int64_t N, int64_t K, void* stream) {
+    if (!is_type(dst)) return QMM_ERR_TYPE;
+    if (dst != QMM_Q8_0 && dst != QMM_Q8_K) return QMM_ERR_UNSUPPORTED;
+    return qmm_quantize(dst, x, xq, N, K, stream);
+}
+
+int qmm_dequantize(int type, const void* blocks, float* out, int64_t rows, int64_t K, void* stream) {
+    if (!is_type(type)) return QMM_ERR_TYPE;
+    int rc;
+    if ((rc = check_ptr(blocks)) || (rc = check_ptr(out))) return rc;
+    if ((rc = check_dims(type, rows, K))) return rc;
+    return hip_status(launch_dequantize(type, blocks, out, rows, K, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+                     int algo, void* stream) {
+    if (!is_type(wtype)) return QMM_ERR_TYPE;
+    if (!is_weight(wtype)) return QMM_ERR_UNSUPPORTED;
+    if (algo < 0 || algo > 2) return QMM_ERR_UNSUPPORTED;
+    int rc;
+    if ((rc = check_ptr(W)) || (rc = check_ptr(xq)) || (rc = check_ptr(y))) return rc;
+    const int xt = qmm_vec_dot_type(wtype);
+    if ((rc = check_dims(wtype, M, K)) || (rc = check_dims(xt, N, K))) return rc;
+    if (M > INT_MAX || N > INT_MAX) return QMM_ERR_SHAPE;
+    if (K > kMaxK) return QMM_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (algo == 2) return QMM_ERR_UNSUPPORTED;  // the MFMA GEMM family is not built yet
+    return hip_status(launch_gemv(wtype, W, xq, y, M, N, K, s));
+}
+
+int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+                void* stream) {
+    return qmm_mul_mat_algo(wtype, W, xq, y, M, N, K, 0, stream);
+}
+
+const char* qmm_strerror(int code) {
+    switch (code) {
+    case QMM_OK: return "ok";
+    case QMM_ERR_TYPE: return "unknown block type";
+    case QMM_ERR_SHAPE: return "invalid shape (size <= 0, K not a multiple of the block size, or too large)";
+    case QMM_ERR_NULL: return "null pointer";
+    case QMM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QMM_ERR_UNSUPPORTED: return "operation not supported for this type or argument";
+    case QMM_ERR_HIP: return "HIP launch error";
+    default: return "unknown status code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// qmm_internal.h — declarations shared by the library's translation units.
+// Host-side launch functions (one per kernel family) and small device helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qmm.h"
+
+namespace qmm {
+
+// Block geometry of the format table (page "The GGML ecosystem, and where
+// synapse fits", §5 "Quantization").
+constexpr int kQ4_0Bytes = 18, kQ8_0Bytes = 34, kQ4_KBytes = 144, kQ6_KBytes = 210, kQ8_KBytes = 292;
+
+__host__ __device__ constexpr int block_size(int t) {
+    return (t == QMM_Q4_0 || t == QMM_Q8_0) ? 32 : (t == QMM_Q4_K || t == QMM_Q6_K || t == QMM_Q8_K) ? 256 : 0;
+}
+__host__ __device__ constexpr int block_bytes(int t) {
+    return t == QMM_Q4_0 ? kQ4_0Bytes : t == QMM_Q8_0 ? kQ8_0Bytes : t == QMM_Q4_K ? kQ4_KBytes
+         : t == QMM_Q6_K ? kQ6_KBytes : t == QMM_Q8_K ? kQ8_KBytes : 0;
+}
+
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+// IEEE binary16 bits -> fp32 (v_cvt_f32_f16: exact, subnormals kept).
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits16 & 0xFFFFu));
+}
+// fp32 -> binary16 bits, round to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint32_t f2h(float f) {
+    return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)f);
+}
+#endif
+
+// ---- launchers (return hipError_t of the launch) ----
+hipError_t launch_quantize(int dst, const float* x, void* out, int64_t rows, int64_t K, hipStream_t s);
+hipError_t launch_dequantize(int t, const void* blocks, float* out, int64_t rows, int64_t K, hipStream_t s);
+hipError_t launch_gemv(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t s);
+hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t s);
+
+}  // namespace qmm

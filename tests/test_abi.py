@@ -1,0 +1,103 @@
+"""The C-ABI library: it loads, exports every function include/qmm.h declares,
+and rejects invalid arguments before launching anything.  None of these calls
+reaches the GPU (validation returns first), so they run without one."""
+import os
+import re
+
+import pytest
+
+import block_quantized_amd as Q
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return Q.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(Q.EXPORTED)
+
+
+def test_sizes(L):
+    assert [Q.qmm_block_size(t) for t in range(1, 6)] == [32, 32, 256, 256, 256]
+    assert [Q.qmm_block_bytes(t) for t in range(1, 6)] == [18, 34, 144, 210, 292]
+    assert Q.qmm_block_size(0) == 0 and Q.qmm_block_bytes(9) == 0
+    assert Q.qmm_row_bytes(Q.QMM_Q4_0, 2048) == 64 * 18
+    assert Q.qmm_row_bytes(Q.QMM_Q6_K, 4096) == 16 * 210
+    assert Q.qmm_row_bytes(Q.QMM_Q4_K, 300) == 0 and Q.qmm_row_bytes(Q.QMM_Q8_0, 0) == 0
+    assert Q.qmm_vec_dot_type(Q.QMM_Q4_0) == Q.QMM_Q8_0
+    assert Q.qmm_vec_dot_type(Q.QMM_Q8_0) == Q.QMM_Q8_0
+    assert Q.qmm_vec_dot_type(Q.QMM_Q4_K) == Q.QMM_Q8_K
+    assert Q.qmm_vec_dot_type(Q.QMM_Q6_K) == Q.QMM_Q8_K
+    assert Q.qmm_vec_dot_type(Q.QMM_Q8_K) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_vec_dot_type(42) == Q.QMM_ERR_TYPE
+    for c in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert isinstance(Q.qmm_strerror(c), str) and Q.qmm_strerror(c)
+
+
+# Fake, never dereferenced device addresses: validation fails before any use.
+A = 0x7F0000000000  # 16-byte aligned
+S = 0  # null stream
+
+
+def test_quantize_errors(L):
+    assert Q.qmm_quantize_act(99, A, A, 1, 32, S) == Q.QMM_ERR_TYPE
+    assert Q.qmm_quantize_act(Q.QMM_Q4_0, A, A, 1, 32, S) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_quantize_act(Q.QMM_Q4_K, A, A, 1, 256, S) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_quantize(Q.QMM_Q6_K, A, A, 1, 256, S) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_quantize_act(Q.QMM_Q8_0, 0, A, 1, 32, S) == Q.QMM_ERR_NULL
+    assert Q.qmm_quantize_act(Q.QMM_Q8_0, A, 0, 1, 32, S) == Q.QMM_ERR_NULL
+    assert Q.qmm_quantize_act(Q.QMM_Q8_0, A + 4, A, 1, 32, S) == Q.QMM_ERR_ALIGN
+    assert Q.qmm_quantize_act(Q.QMM_Q8_0, A, A + 2, 1, 32, S) == Q.QMM_ERR_ALIGN
+    assert Q.qmm_quantize_act(Q.QMM_Q8_0, A, A, 0, 32, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_quantize_act(Q.QMM_Q8_0, A, A, 1, 48, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_quantize_act(Q.QMM_Q8_K, A, A, 1, 128, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_quantize_act(Q.QMM_Q8_K, A, A, -5, 256, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_quantize_act(Q.QMM_Q8_K, A, A, 2 ** 62, 256, S) == Q.QMM_ERR_SHAPE
+
+
+def test_dequantize_errors(L):
+    assert Q.qmm_dequantize(0, A, A, 1, 32, S) == Q.QMM_ERR_TYPE
+    assert Q.qmm_dequantize(Q.QMM_Q4_K, A, A, 1, 32, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_dequantize(Q.QMM_Q4_0, 0, A, 1, 32, S) == Q.QMM_ERR_NULL
+    assert Q.qmm_dequantize(Q.QMM_Q4_0, A, A + 8, 1, 32, S) == Q.QMM_ERR_ALIGN
+
+
+def test_mul_mat_errors(L):
+    mm = Q.qmm_mul_mat
+    assert mm(77, A, A, A, 4, 1, 256, S) == Q.QMM_ERR_TYPE
+    assert mm(Q.QMM_Q8_K, A, A, A, 4, 1, 256, S) == Q.QMM_ERR_UNSUPPORTED
+    assert mm(Q.QMM_Q4_K, 0, A, A, 4, 1, 256, S) == Q.QMM_ERR_NULL
+    assert mm(Q.QMM_Q4_K, A, 0, A, 4, 1, 256, S) == Q.QMM_ERR_NULL
+    assert mm(Q.QMM_Q4_K, A, A, 0, 4, 1, 256, S) == Q.QMM_ERR_NULL
+    assert mm(Q.QMM_Q4_K, A + 2, A, A, 4, 1, 256, S) == Q.QMM_ERR_ALIGN
+    assert mm(Q.QMM_Q4_K, A, A, A + 4, 4, 1, 256, S) == Q.QMM_ERR_ALIGN
+    assert mm(Q.QMM_Q4_K, A, A, A, 4, 1, 128, S) == Q.QMM_ERR_SHAPE   # K % 256
+    assert mm(Q.QMM_Q4_0, A, A, A, 4, 1, 48, S) == Q.QMM_ERR_SHAPE    # K % 32
+    assert mm(Q.QMM_Q4_0, A, A, A, 0, 1, 32, S) == Q.QMM_ERR_SHAPE
+    assert mm(Q.QMM_Q4_0, A, A, A, 4, 0, 32, S) == Q.QMM_ERR_SHAPE
+    assert mm(Q.QMM_Q4_0, A, A, A, 2 ** 31, 1, 32, S) == Q.QMM_ERR_SHAPE
+    assert mm(Q.QMM_Q6_K, A, A, A, 4, 1, 65536 + 256, S) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_mul_mat_algo(Q.QMM_Q4_0, A, A, A, 4, 1, 32, 3, S) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_mul_mat_algo(Q.QMM_Q4_0, A, A, A, 4, 1, 32, -1, S) == Q.QMM_ERR_UNSUPPORTED
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    # With the library path pointing nowhere, loading must raise, not degrade.
+    monkeypatch.setattr(Q, "_lib", None)
+    monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        Q.lib()
