@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized product on one MI355X.
+
+Headline (`value`): GEMV effective GB/s at batch 1 on the Q4_0 x Q8_0 decode
+workload with 1B-Llama layer shapes: one step is one decode token's worth of
+the hot path through 16 layers, each layer
+    quantize x (K=2048) -> GEMV attn_q 2048x2048, attn_k 512x2048, attn_v 512x2048
+    quantize x (K=2048) -> GEMV attn_output 2048x2048
+    quantize x (K=2048) -> GEMV ffn_gate 8192x2048, ffn_up 8192x2048
+    quantize x (K=8192) -> GEMV ffn_down 2048x8192
+(the quantizes stand where the model's activations change; what runs between
+them in a model - attention, norms, SwiGLU - is outside this library).  The
+step is captured once in a HIP graph and replayed.  547 MB of weights per step
+exceed the 256 MB Infinity Cache, so every step streams W from HBM.
+Bytes are algorithmic: W blocks + quantized activations + fp32 outputs of
+every GEMV, plus fp32 in / blocks out of every quantize.
+
+Also reported: the int8 GEMM rate at batch 512 (Q4_K 4096x4096 and 14336x4096
+prefill), the other GEMV workloads, the dominant kernel's roofline from HIP
+events, and the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
+METRIC = "GEMV effective GB/s (% HBM peak) at batch 1; GEMM int8 TOPS at batch 512"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--quick", action="store_true", help="headline only (no secondary workloads)")
+    return p.parse_args()
+
+
+class Bench:
+    def __init__(self):
+        import torch
+
+        import block_quantized_amd as Q
+        if not os.path.exists(Q.LIB_PATH):
+            from block_quantized_amd import build
+            build.build()
+        Q.lib()
+        self.torch, self.Q = torch, Q
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.Stream()
+
+    # -- helpers ---------------------------------------------------------
+    def call(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: {self.Q.qmm_strerror(rc)}")
+
+    def graph(self, fn):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        self.stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.stream):
+            fn()  # eager warm-up outside the capture
+        torch.cuda.current_stream().wait_stream(self.stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=self.stream):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(self, g, reps, warmup):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for _ in range(warmup):
+                g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            t0.record(self.stream)
+            for _ in range(reps):
+                g.replay()
+            t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / 1e3  # seconds
+
+    def gpu_u8(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+
+# ---------------------------------------------------------------- headline
+
+def decode_sweep(b: Bench, steps: int, warmup: int, keep_cpu_layers: int):
+    import synth
+    torch, Q = b.torch, b.Q
+    g = synth.rng(0)
+    layers, cpu_f32 = [], []
+    for li in range(synth.LLAMA_1B_LAYERS):
+        L = {}
+        for name, M, K in synth.LLAMA_1B_LAYER:
+            wf = synth.normal_f32(g, (M, K), 0.02)
+            if li < keep_cpu_layers:
+                cpu_f32.append((li, name, wf))
+            wg = torch.from_numpy(wf).to(b.dev)
+            blocks = torch.empty((M, Q.qmm_row_bytes(Q.QMM_Q4_0, K)), dtype=torch.uint8, device=b.dev)
+            b.call(Q.qmm_quantize(Q.QMM_Q4_0, wg, blocks, M, K, 0), "quantize W")
+            L[name] = (blocks, M, K)
+            del wg
+        layers.append(L)
+    torch.cuda.synchronize()
+    xs = []
+    for li in range(synth.LLAMA_1B_LAYERS):
+        xs.append({k: torch.from_numpy(synth.normal_f32(g, (1, K), 1.0)).to(b.dev)
+                   for k, K in (("attn", 2048), ("o", 2048), ("ffn", 2048), ("down", 8192))})
+    xq = {K: torch.empty((1, Q.qmm_row_bytes(Q.QMM_Q8_0, K)), dtype=torch.uint8, device=b.dev)
+          for K in (2048, 8192)}
+    ys = {name: torch.empty((1, M), dtype=torch.float32, device=b.dev) for name, M, K in synth.LLAMA_1B_LAYER}
+
+    stages = (("attn", ("attn_q", "attn_k", "attn_v")), ("o", ("attn_output",)),
+              ("ffn", ("ffn_gate", "ffn_up")), ("down", ("ffn_down",)))
+    gemv_calls, quant_calls = [], []
+    for li, L in enumerate(layers):
+        for xname, mats in stages:
+            x = xs[li][xname]
+            K = x.shape[1]
+            quant_calls.append((x.data_ptr(), xq[K].data_ptr(), K))
+            for m in mats:
+                blocks, M, KK = L[m]
+                gemv_calls.append((blocks.data_ptr(), xq[K].data_ptr(), ys[m].data_ptr(), M, KK, len(quant_calls) - 1))
+
+    lib = Q.lib()
+
+    def step():
+        s = torch.cuda.current_stream().cuda_stream
+        qi = 0
+        for (w, xp, yp, M, K, qidx) in gemv_calls:
+            while qi <= qidx:
+                x, o, KK = quant_calls[qi]
+                rc = lib.qmm_quantize_act(Q.QMM_Q8_0, x, o, 1, KK, s)
+                if rc:
+                    raise RuntimeError(Q.qmm_strerror(rc))
+                qi += 1
+            rc = lib.qmm_mul_mat(Q.QMM_Q4_0, w, xp, yp, M, 1, K, s)
+            if rc:
+                raise RuntimeError(Q.qmm_strerror(rc))
+
+    def gemv_only():
+        s = torch.cuda.current_stream().cuda_stream
+        for (w, xp, yp, M, K, _) in gemv_calls:
+            lib.qmm_mul_mat(Q.QMM_Q4_0, w, xp, yp, M, 1, K, s)
+
+    def gemv_bytes(M, K):
+        return M * (K // 32) * 18 + (K // 32) * 34 + 4 * M
+
+    bytes_gemv = sum(gemv_bytes(M, K) for (_, _, _, M, K, _) in gemv_calls)
+    bytes_quant = sum(4 * K + (K // 32) * 34 for (_, _, K) in quant_calls)
+    bytes_step = bytes_gemv + bytes_quant
+    w_bytes = sum(M * (K // 32) * 18 for (_, _, _, M, K, _) in gemv_calls)
+
+    g_step = b.graph(step)
+    sec = b.time_graph(g_step, steps, warmup)
+    g_gemv = b.graph(gemv_only)
+    sec_gemv = b.time_graph(g_gemv, steps, warmup)
+    res = {
+        "bytes_step": bytes_step, "w_bytes": w_bytes, "seconds": sec, "steps": steps,
+        "gbs": bytes_step * steps / sec / 1e9, "ms_per_step": sec / steps * 1e3,
+        "gemv_launches_per_step": len(gemv_calls), "quantize_launches_per_step": len(quant_calls),
+        "gemv_bytes_per_step": bytes_gemv, "gemv_seconds": sec_gemv,
+        "gemv_gbs": bytes_gemv * steps / sec_gemv / 1e9,
+    }
+    return res, cpu_f32
+
+
+def cpu_baseline_decode(cpu_f32, min_seconds=10.0):
+    """The oracle (as it stands) on layers 0..L-1 of the same workload."""
+    import oracle as O
+    import synth
+    g = synth.rng(12345)
+    mats = [(name, O.quantize(O.Q4_0, wf), wf.shape[0], wf.shape[1]) for (_, name, wf) in cpu_f32]
+    layers = sorted({li for (li, _, _) in cpu_f32})
+    xs = [synth.normal_f32(g, (1, K), 1.0) for K in (2048, 2048, 2048, 8192)] * len(layers)
+    per_rep_bytes = 0
+    for name, W, M, K in mats:
+        per_rep_bytes += W.nbytes + (K // 32) * 34 + 4 * M
+    per_rep_bytes += sum(4 * x.shape[1] + (x.shape[1] // 32) * 34 for x in xs)
+    stage_of = {"attn_q": 0, "attn_k": 0, "attn_v": 0, "attn_output": 1, "ffn_gate": 2, "ffn_up": 2, "ffn_down": 3}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        xq = [O.quantize(O.Q8_0, x) for x in xs]
+        for i, (name, W, M, K) in enumerate(mats):
+            li = i // 7
+            O.mul_mat(O.Q4_0, W, xq[4 * li + stage_of[name]], M, 1, K, with_T=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": per_rep_bytes * reps / el / 1e9, "unit": "GB/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"layers 0-{len(layers) - 1} of the same 16-layer Q4_0 decode sweep "
+                      f"({per_rep_bytes / 1e6:.1f} MB per pass), oracle quantize + fp64 product, "
+                      f"{reps} passes in {el:.1f} s"}
+
+
+# ------------------------------------------------------- secondary loads
+
+def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=8):
+    """Per-launch time of one GEMV shape, rotating through copies of W so the
+    total exceeds the 256 MB Infinity Cache (every launch reads HBM)."""
+    import oracle as O
+    import synth
+    torch, Q = b.torch, b.Q
+    g = synth.rng(0)
+    W = make_w(g, M, K)
+    wbytes = W.nbytes
+    copies = max(1, int(np.ceil(min_bytes / wbytes)))
+    Wg = [b.gpu_u8(W)]
+    for _ in range(copies - 1):
+        Wg.append(Wg[0].clone())
+    x = synth.normal_f32(g, (N, K), 1.0)
+    xt = O.VEC_DOT_TYPE[wtype]
+    xq = torch.empty((N, Q.qmm_row_bytes(xt, K)), dtype=torch.uint8, device=b.dev)
+    b.call(Q.qmm_quantize_act(xt, b.torch.from_numpy(x).to(b.dev), xq, N, K, 0), "quantize x")
+    y = torch.empty((N, M), dtype=torch.float32, device=b.dev)
+    lib = Q.lib()
+
+    def run():
+        s = torch.cuda.current_stream().cuda_stream
+        for w in Wg:
+            lib.qmm_mul_mat(wtype, w.data_ptr(), xq.data_ptr(), y.data_ptr(), M, N, K, s)
+
+    gr = b.graph(run)
+    reps = max(reps_floor, int(np.ceil(4e9 / (wbytes * copies))))
+    sec = b.time_graph(gr, reps, 2)
+    launches = reps * copies
+    alg = wbytes + xq.numel() + 4 * N * M
+    del Wg
+    torch.cuda.empty_cache()
+    return {"us_per_launch": sec / launches * 1e6, "bytes_per_launch": alg,
+            "gbs": alg * launches / sec / 1e9, "frac_hbm": alg * launches / sec / 1e9 / HBM_PEAK_GBS,
+            "tops": 2 * M * N * K * launches / sec / 1e12, "copies": copies}
+
+
+def secondary(b: Bench):
+    import oracle as O
+    import synth
+    out = {}
+    q80 = lambda g, M, K: O.quantize(O.Q8_0, synth.normal_f32(g, (M, K), 0.02))
+    out["q8_0_gemv_2048x2048_b1"] = gemv_workload(b, b.Q.QMM_Q8_0, 2048, 2048, 1, q80)
+    for (M, K) in synth.LLAMA_8B_SHAPES:
+        for N in (1, 4, 8):
+            out[f"q4_k_gemv_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q4_K, M, K, N, synth.q4_k_random)
+    M, K = synth.LLAMA_8B_HEAD
+    for N in (1, 32):
+        out[f"q6_k_head_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q6_K, M, K, N, synth.q6_k_random,
+                                                     min_bytes=1, reps_floor=20)
+    for M in (4096, 14336):
+        r = gemv_workload(b, b.Q.QMM_Q4_K, M, 4096, 512, synth.q4_k_random, min_bytes=1, reps_floor=5)
+        r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
+        out[f"q4_k_gemm_{M}x4096_b512"] = r
+    return out
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the product shards by output "
+              "rows with no exchange, so N GPUs would each run this workload on M/N rows.", file=sys.stderr)
+        sys.exit(2)
+    b = Bench()
+    head, cpu_f32 = decode_sweep(b, a.steps, a.warmup, keep_cpu_layers=0 if a.no_cpu else 2)
+    gemv_us = head["gemv_seconds"] / (a.steps * head["gemv_launches_per_step"]) * 1e6
+    line = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "Q4_0 x Q8_0 decode GEMV, batch 1, 1B-Llama layer shapes (attn_q/attn_output "
+                        "2048x2048, attn_k/attn_v 512x2048, ffn_gate/ffn_up 8192x2048, ffn_down 2048x8192) "
+                        "x 16 layers, W ~ N(0,0.02) quantized to Q4_0, x ~ N(0,1) quantized to Q8_0, seed 0",
+            "bytes_per_step": head["bytes_step"],
+            "weight_bytes_per_step": head["w_bytes"],
+            "launches_per_step": head["gemv_launches_per_step"] + head["quantize_launches_per_step"],
+            "frac_hbm_peak": round(head["gbs"] / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_kernel<Q4_0, 1 column>",
+            "achieved": round(head["gemv_gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["gemv_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(gemv_us, 3),
+            "launches": head["gemv_launches_per_step"] * a.steps,
+        },
+    }
+    if not a.quick:
+        sec = secondary(b)
+        line["secondary"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                             for k, v in sec.items()}
+        gm = [sec[k] for k in sec if k.startswith("q4_k_gemm")]
+        line["gemm_int8_tops_batch512"] = {
+            "value": round(min(r["tops"] for r in gm), 2), "unit": "TOPS",
+            "per_shape": {k: round(v["tops"], 2) for k, v in sec.items() if k.startswith("q4_k_gemm")},
+            "peak": INT8_PEAK_TOPS,
+        }
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_decode(cpu_f32)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
