@@ -11,54 +11,65 @@
 //                two 16-wide sums of sub-block j)
 //   Q6_K x Q8_K: dx * d * sum_j sc_j (sum q_w q_x - 32 S_j)          (S_j: 16-wide sum)
 // (the Q6_K offset 32 is this library's reading of the format table).
-// Decode speed is bound by streaming the weights from memory (page "llama.cpp
-// and GGUF", "The ggml Tensor Library and Backends": decode speed tracks memory
+// Decode speed is bound by streaming W from memory (page "llama.cpp and
+// GGUF", "The ggml Tensor Library and Backends": decode speed tracks memory
 // bandwidth), so the kernel is organised around moving W at full HBM rate:
 //
-//  * The unit of work of one lane is 256 consecutive weights of one row
-//    ("unit": 144 B of Q4_0 or Q4_K, 272 B of Q8_0, 210 B of Q6_K).  A row of
-//    K weights is G = K/256 units.  P = next power of two >= min(G, 64)
-//    lanes share a row; a wavefront covers RW = 64/P whole rows per "chunk",
-//    or, when G > 64, a row in ceil(G/64) chunks of 64 units.  A chunk is one
-//    contiguous byte range of W.
-//  * Chunks are read with coalesced 16-byte loads (lane l reads bytes
-//    16(l + 64j)), one chunk ahead of the compute, into VGPRs; the chunk is
-//    then written to the wavefront's private LDS slot, where each lane reads
-//    its own unit back.  No workgroup barrier is needed in the main loop.
+//  * A lane's unit of work is a run of consecutive weights of one row,
+//    16-byte aligned, loaded by that lane alone with 16-byte loads straight
+//    into registers: 256 weights (8 blocks, 144 B) for Q4_0, 256 (8 blocks,
+//    272 B) for Q8_0, one 144 B super-block for Q4_K, and 8 super-blocks
+//    (1680 B) for Q6_K, whose 210 B super-blocks are only 2-byte aligned:
+//    its j-th super-block starts 2j bytes past a 16-byte boundary, so each
+//    of the 8 sub-steps reads a 224 B window whose skew is a compile-time
+//    constant.  (Measured on MI355X: per-lane 144 B units stream as fast as
+//    fully coalesced reads, ~6.3 TB/s; staging through LDS halved that.)
+//  * Loads run one step ahead (two register buffers), and the first step's
+//    loads are issued before the activations are staged.
+//  * A row of K weights is GU units; P = next power of two >= min(GU, 64)
+//    lanes share a row, a wavefront covers RW = 64/P rows per chunk, or a
+//    row in ceil(GU/64) chunks when GU > 64.  Lanes of a row are reduced with
+//    a fixed butterfly, so results are bit-identical run to run.
+//  * Several matrices sharing K and x (e.g. q|k|v, gate|up) can form one
+//    launch: their chunks are concatenated ("segments").
 //  * The activations (N rows of Q8_0 or Q8_K blocks) are repacked once per
-//    workgroup into LDS records of 336 bytes per (row, 256-value group):
-//    256 int8 codes, then the fp32 scales and precomputed integer sums.  The
-//    record stride (84 dwords) keeps 16-byte LDS reads of consecutive groups
-//    on distinct banks.
-//  * Workgroups are persistent: each wavefront walks chunks with a grid
-//    stride; lanes of a row are reduced with a fixed butterfly, so results
-//    are bit-identical run to run.
+//    workgroup into LDS records of 336 bytes per (row, 256-value group): 256
+//    int8 codes, then the fp32 scales and precomputed integer sums.
 #include "qmm_internal.h"
 
 namespace qmm {
 namespace {
 
-template <int WT> struct GFmt;
-template <> struct GFmt<QMM_Q4_0> { static constexpr int UB = 144, NJ = 9; };
-template <> struct GFmt<QMM_Q8_0> { static constexpr int UB = 272, NJ = 17; };
-template <> struct GFmt<QMM_Q4_K> { static constexpr int UB = 144, NJ = 9; };
-template <> struct GFmt<QMM_Q6_K> { static constexpr int UB = 210, NJ = 14; };  // 13440 B + up to 14 B skew
+template <int WT> struct U;
+template <> struct U<QMM_Q4_0> { static constexpr int UB = 144, NV = 9, SUB = 1, WPU = 256; };
+template <> struct U<QMM_Q8_0> { static constexpr int UB = 272, NV = 17, SUB = 1, WPU = 256; };
+template <> struct U<QMM_Q4_K> { static constexpr int UB = 144, NV = 9, SUB = 1, WPU = 256; };
+template <> struct U<QMM_Q6_K> { static constexpr int UB = 8 * kQ6_KBytes, NV = 14, SUB = 8, WPU = 2048; };
+
+template <int J, int B> struct Tag { static constexpr int j = J, b = B; };
 
 constexpr int XREC = 336;  // LDS bytes per (activation row, 256-value group)
+constexpr int kMaxSeg = 4;
+
+struct Seg {
+    const uint8_t* W;
+    float* y;
+    int64_t M;
+    int64_t work0;  // first work item of this segment in the launch
+};
+// y of a segment is N x M (row stride M)
 
 struct GemvArgs {
-    const uint8_t* W;
+    Seg seg[kMaxSeg];
+    int nseg;
     const uint8_t* xq;
-    float* y;
-    int64_t M;        // rows of W (and columns of y)
-    int64_t rowB;     // bytes per W row
-    int64_t total;    // bytes of W
-    int64_t nwork;    // work items (row sets)
-    int64_t ldy;      // row stride of y (= M of the full problem)
-    int G;            // 256-weight units per row
-    int logP;         // log2(lanes per row)
-    int RW;           // rows per chunk
-    int nkc;          // chunks per work item
+    int64_t rowB;      // bytes per W row
+    int64_t nwork;     // work items over all segments
+    int G;             // 256-value activation groups per row (K / 256)
+    int GU;            // lane units per row
+    int logP;          // log2(lanes per row)
+    int RW;            // rows per chunk
+    int nkc;           // chunks per work item
 };
 
 __device__ __forceinline__ uint32_t ld_u16x2_g(const uint8_t* p) {
@@ -71,71 +82,112 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
 }
 
 // ---------------------------------------------------- activation staging
+// Each thread owns whole staging items: one 34 B Q8_0 block, or a quarter of
+// a 292 B Q8_K block.  All of a round's global loads are issued before any
+// LDS store, so a round costs one memory round trip; `after_loads` runs once,
+// right after the first round's loads (the W prefetch goes there, so waiting
+// for x - loads retire in order - does not wait for W).  The activation rows
+// are contiguous, so item i's bytes follow item i-1's.
 
-template <int WT, int NC>
-__device__ void stage_x(const GemvArgs& a, uint8_t* xl) {
-    const int G = a.G;
-    if constexpr (WT == QMM_Q4_0 || WT == QMM_Q8_0) {
-        // Q8_0 activations: group g of row n = blocks 8g..8g+7 (34 B each).
-        const int64_t xrow = (int64_t)G * 8 * kQ8_0Bytes;
-        for (int i = threadIdx.x; i < NC * G * 64; i += blockDim.x) {
-            const int n = i / (G * 64), r = i - n * G * 64, g = r >> 6, qd = r & 63;
-            const uint8_t* blk = a.xq + n * xrow + (int64_t)(8 * g + (qd >> 3)) * kQ8_0Bytes;
-            reinterpret_cast<uint32_t*>(xl + (n * G + g) * XREC)[qd] = ld_u16x2_g(blk + 2 + 4 * (qd & 7));
-        }
-        for (int i = threadIdx.x; i < NC * G * 8; i += blockDim.x) {
-            const int n = i / (G * 8), r = i - n * G * 8, g = r >> 3, bi = r & 7;
-            const uint8_t* blk = a.xq + n * xrow + (int64_t)(8 * g + bi) * kQ8_0Bytes;
-            uint32_t* rec = reinterpret_cast<uint32_t*>(xl + (n * G + g) * XREC);
-            reinterpret_cast<float*>(rec)[64 + bi] = h2f(reinterpret_cast<const uint16_t*>(blk)[0]);
-            int s = 0;
+template <int WT, int NC, class Hook>
+__device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, Hook&& after_loads) {
+    constexpr bool kQ80 = (WT == QMM_Q4_0 || WT == QMM_Q8_0);
+    constexpr int KB = 4;  // items per thread per round
+    const int nitems = kQ80 ? NC * G * 8 : NC * G * 4;
+    const int step = KB * blockDim.x;
+    for (int base = 0, round = 0; base < nitems || round == 0; base += step, ++round) {
+        if constexpr (kQ80) {
+            uint32_t v[KB][17];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) s = dot4(ld_u16x2_g(blk + 2 + 4 * k), 0x01010101u, s);
-            reinterpret_cast<int*>(rec)[72 + bi] = 8 * s;  // Q4_0's offset term: 8 * sum q_x
-        }
-    } else {
-        // Q8_K activations: group g of row n = block g (292 B).
-        const int64_t xrow = (int64_t)G * kQ8_KBytes;
-        for (int i = threadIdx.x; i < NC * G * 64; i += blockDim.x) {
-            const int n = i / (G * 64), r = i - n * G * 64, g = r >> 6, qd = r & 63;
-            const uint8_t* blk = a.xq + n * xrow + (int64_t)g * kQ8_KBytes;
-            reinterpret_cast<uint32_t*>(xl + (n * G + g) * XREC)[qd] =
-                reinterpret_cast<const uint32_t*>(blk + 4)[qd];
-        }
-        constexpr int NM = (WT == QMM_Q4_K) ? 8 : 16;
-        for (int i = threadIdx.x; i < NC * G * (NM + 1); i += blockDim.x) {
-            const int n = i / (G * (NM + 1)), r = i - n * G * (NM + 1), g = r / (NM + 1), j = r % (NM + 1);
-            const uint8_t* blk = a.xq + n * xrow + (int64_t)g * kQ8_KBytes;
-            uint32_t* rec = reinterpret_cast<uint32_t*>(xl + (n * G + g) * XREC);
-            const int16_t* bs = reinterpret_cast<const int16_t*>(blk + 260);
-            if (j == NM) {
-                rec[64] = reinterpret_cast<const uint32_t*>(blk)[0];  // fp32 d
-            } else if (WT == QMM_Q4_K) {
-                reinterpret_cast<int*>(rec)[65 + j] = (int)bs[2 * j] + (int)bs[2 * j + 1];
-            } else {
-                reinterpret_cast<int*>(rec)[65 + j] = 32 * (int)bs[j];
+            for (int k = 0; k < KB; ++k) {
+                const int i = base + k * blockDim.x + threadIdx.x;
+                if (i < nitems) {
+                    const uint16_t* p = reinterpret_cast<const uint16_t*>(xq + (int64_t)i * kQ8_0Bytes);
+#pragma unroll
+                    for (int h = 0; h < 17; ++h) v[k][h] = p[h];
+                }
+            }
+            if (round == 0) after_loads();
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int i = base + k * blockDim.x + threadIdx.x;
+                if (i < nitems) {
+                    uint8_t* rec = xl + (i >> 3) * XREC;
+                    const int bi = i & 7;
+                    uint32_t q[8];
+                    int sx = 0;
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) {
+                        q[d] = v[k][1 + 2 * d] | (v[k][2 + 2 * d] << 16);
+                        sx = dot4(q[d], 0x01010101u, sx);
+                    }
+                    reinterpret_cast<uint4*>(rec + 32 * bi)[0] = make_uint4(q[0], q[1], q[2], q[3]);
+                    reinterpret_cast<uint4*>(rec + 32 * bi)[1] = make_uint4(q[4], q[5], q[6], q[7]);
+                    reinterpret_cast<float*>(rec)[64 + bi] = h2f(v[k][0]);
+                    reinterpret_cast<int*>(rec)[72 + bi] = 8 * sx;  // Q4_0's offset term: 8 * sum q_x
+                }
+            }
+        } else {
+            uint32_t v[KB][19];
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int i = base + k * blockDim.x + threadIdx.x;
+                if (i < nitems) {
+                    const uint32_t* p = reinterpret_cast<const uint32_t*>(xq + (int64_t)(i >> 2) * kQ8_KBytes);
+                    const int qq = i & 3;
+#pragma unroll
+                    for (int d = 0; d < 16; ++d) v[k][d] = p[1 + 16 * qq + d];
+                    v[k][16] = p[65 + 2 * qq];  // bsums 4qq .. 4qq+3
+                    v[k][17] = p[66 + 2 * qq];
+                    v[k][18] = p[0];            // fp32 d
+                }
+            }
+            if (round == 0) after_loads();
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int i = base + k * blockDim.x + threadIdx.x;
+                if (i < nitems) {
+                    uint8_t* rec = xl + (i >> 2) * XREC;
+                    const int qq = i & 3;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        reinterpret_cast<uint4*>(rec + 64 * qq)[d] =
+                            make_uint4(v[k][4 * d], v[k][4 * d + 1], v[k][4 * d + 2], v[k][4 * d + 3]);
+                    const int b0 = (int16_t)(v[k][16] & 0xFFFF), b1 = (int16_t)(v[k][16] >> 16);
+                    const int b2 = (int16_t)(v[k][17] & 0xFFFF), b3 = (int16_t)(v[k][17] >> 16);
+                    int* meta = reinterpret_cast<int*>(rec) + 65;
+                    if constexpr (WT == QMM_Q4_K) {  // sums over the 32-wide sub-blocks 2qq, 2qq+1
+                        meta[2 * qq] = b0 + b1;
+                        meta[2 * qq + 1] = b2 + b3;
+                    } else {                         // 32 * (16-wide sums) 4qq .. 4qq+3
+                        meta[4 * qq] = 32 * b0;
+                        meta[4 * qq + 1] = 32 * b1;
+                        meta[4 * qq + 2] = 32 * b2;
+                        meta[4 * qq + 3] = 32 * b3;
+                    }
+                    if (qq == 0) reinterpret_cast<uint32_t*>(rec)[64] = v[k][18];
+                }
             }
         }
     }
 }
 
 // ------------------------------------------------------- unit compute
+// w: the unit's bytes as dwords (registers); xr0: LDS record of activation
+// row 0 for this unit's first 256-value group; xstride: LDS bytes between
+// activation rows.
 
 template <int NC>
-__device__ __forceinline__ void unit_q4_0(const uint32_t* __restrict__ u, const uint8_t* xr0, int xstride,
-                                          float (&acc)[NC]) {
-    uint32_t w[36];
-#pragma unroll
-    for (int i = 0; i < 9; ++i) reinterpret_cast<uint4*>(w)[i] = reinterpret_cast<const uint4*>(u)[i];
+__device__ __forceinline__ void unit_q4_0(const uint32_t* w, const uint8_t* xr0, int xstride, float (&acc)[NC]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         uint32_t db, q[4];
-        if ((i & 1) == 0) {
+        if ((i & 1) == 0) {  // block at byte 18i = 4b: d in the low half of w[b]
             const int b = 9 * i / 2;
             db = w[b];
 #pragma unroll
             for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_alignbyte(w[b + k + 1], w[b + k], 2);
-        } else {
+        } else {             // block at byte 4b + 2: d in the high half of w[b]
             const int b = 9 * (i - 1) / 2 + 4;
             db = w[b] >> 16;
 #pragma unroll
@@ -165,24 +217,20 @@ __device__ __forceinline__ void unit_q4_0(const uint32_t* __restrict__ u, const 
 }
 
 template <int NC>
-__device__ __forceinline__ void unit_q8_0(const uint32_t* __restrict__ u, const uint8_t* xr0, int xstride,
-                                          float (&acc)[NC]) {
+__device__ __forceinline__ void unit_q8_0(const uint32_t* w, const uint8_t* xr0, int xstride, float (&acc)[NC]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         uint32_t db, q[8];
-        if ((i & 1) == 0) {
+        if ((i & 1) == 0) {  // block at byte 34i = 4b
             const int b = 17 * i / 2;
-            uint32_t w[9];
+            db = w[b];
 #pragma unroll
-            for (int k = 0; k < 9; ++k) w[k] = u[b + k];
-            db = w[0];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) q[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], 2);
-        } else {
+            for (int k = 0; k < 8; ++k) q[k] = __builtin_amdgcn_alignbyte(w[b + k + 1], w[b + k], 2);
+        } else {             // block at byte 4b + 2
             const int b = (17 * i - 1) / 2;
-            db = u[b] >> 16;
+            db = w[b] >> 16;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) q[k] = u[b + 1 + k];
+            for (int k = 0; k < 8; ++k) q[k] = w[b + 1 + k];
         }
         const float dw = h2f(db);
 #pragma unroll
@@ -198,22 +246,17 @@ __device__ __forceinline__ void unit_q8_0(const uint32_t* __restrict__ u, const 
 }
 
 template <int NC>
-__device__ __forceinline__ void unit_q4_k(const uint32_t* __restrict__ u, const uint8_t* xr0, int xstride,
-                                          float (&acc)[NC]) {
-    const uint4 h = reinterpret_cast<const uint4*>(u)[0];
-    const float d = h2f(h.x), dmin = h2f(h.x >> 16);
+__device__ __forceinline__ void unit_q4_k(const uint32_t* w, const uint8_t* xr0, int xstride, float (&acc)[NC]) {
+    const float d = h2f(w[0]), dmin = h2f(w[0] >> 16);
     // eight 6-bit scales and mins, one per byte
-    const uint32_t sc03 = h.y & 0x3F3F3F3Fu, m03 = h.z & 0x3F3F3F3Fu;
-    const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
-    const uint32_t m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+    const uint32_t sc03 = w[1] & 0x3F3F3F3Fu, m03 = w[2] & 0x3F3F3F3Fu;
+    const uint32_t sc47 = (w[3] & 0x0F0F0F0Fu) | ((w[1] >> 2) & 0x30303030u);
+    const uint32_t m47 = ((w[3] >> 4) & 0x0F0F0F0Fu) | ((w[2] >> 2) & 0x30303030u);
     int sumi[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) sumi[n] = 0;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        uint32_t q[8];
-        reinterpret_cast<uint4*>(q)[0] = reinterpret_cast<const uint4*>(u)[1 + 2 * g];
-        reinterpret_cast<uint4*>(q)[1] = reinterpret_cast<const uint4*>(u)[2 + 2 * g];
+    for (int g = 0; g < 4; ++g) {  // sub-blocks 2g (low nibbles) and 2g+1 (high nibbles)
         const uint32_t scw = (g < 2) ? sc03 : sc47;
         const int sc_lo = (scw >> (16 * (g & 1))) & 0xFF, sc_hi = (scw >> (16 * (g & 1) + 8)) & 0xFF;
 #pragma unroll
@@ -222,8 +265,9 @@ __device__ __forceinline__ void unit_q4_k(const uint32_t* __restrict__ u, const 
             int dl = 0, dh = 0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                dl = dot4(q[k] & 0x0F0F0F0Fu, xr[16 * g + k], dl);
-                dh = dot4((q[k] >> 4) & 0x0F0F0F0Fu, xr[16 * g + 8 + k], dh);
+                const uint32_t q = w[4 + 8 * g + k];
+                dl = dot4(q & 0x0F0F0F0Fu, xr[16 * g + k], dl);
+                dh = dot4((q >> 4) & 0x0F0F0F0Fu, xr[16 * g + 8 + k], dh);
             }
             sumi[n] += sc_lo * dl + sc_hi * dh;
         }
@@ -243,20 +287,21 @@ __device__ __forceinline__ void unit_q4_k(const uint32_t* __restrict__ u, const 
     }
 }
 
-template <int NC>
-__device__ __forceinline__ void unit_q6_k(const uint32_t* __restrict__ ubase, int uoff, const uint8_t* xr0,
-                                          int xstride, float (&acc)[NC]) {
-    // The super-block starts at an even byte offset; read whole dwords and
-    // shift by 0 or 16 bits.
-    const uint32_t* u = ubase + (uoff >> 2);
-    const uint32_t sh = (uint32_t)(uoff & 2) * 8;
-    auto W = [&](int i) { return __builtin_amdgcn_alignbit(u[i + 1], u[i], sh); };
+// One Q6_K super-block whose first byte is byte SKEW of the window r (SKEW
+// even, 0..14): dword i of the super-block is bytes SKEW + 4i .. of r.
+template <int NC, int SKEW>
+__device__ __forceinline__ void unit_q6_k(const uint32_t* r, const uint8_t* xr0, int xstride, float (&acc)[NC]) {
+    constexpr int o = SKEW >> 2;
+    auto W = [&](int i) -> uint32_t {
+        if constexpr ((SKEW & 3) == 0) return r[o + i];
+        else return __builtin_amdgcn_alignbyte(r[o + i + 1], r[o + i], 2);
+    };
     const float dw = h2f(W(52));
     int isum[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) isum[n] = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 16; ++j) {  // 16-wide sub-blocks
         const int h = j >> 3, c = (j >> 1) & 3, kk = j & 1;
         const int sc = __builtin_amdgcn_sbfe((int)W(48 + (j >> 2)), 8 * (j & 3), 8);
         uint32_t q[4];
@@ -287,163 +332,239 @@ __device__ __forceinline__ void unit_q6_k(const uint32_t* __restrict__ ubase, in
 
 // ------------------------------------------------------------- kernel
 
-template <int WT, int NC, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
-    using F = GFmt<WT>;
-    constexpr int UB = F::UB, NJ = F::NJ, SLOT = NJ * 1024;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* xl = smem + WAVES * SLOT;
+template <int WT, int NC>
+__global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
+    using F = U<WT>;
+    constexpr int NV = F::NV, SUB = F::SUB;
+    extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
 
-    stage_x<WT, NC>(a, xl);
-    __syncthreads();
-
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * WAVES + wave, TW = (int64_t)gridDim.x * WAVES;
-    if (gw >= a.nwork) return;  // no barrier follows
-    uint8_t* slot = smem + wave * SLOT;
-    const int64_t nch = ((a.nwork - 1 - gw) / TW + 1) * a.nkc;
-    const int P = 1 << a.logP;
-
-    // byte range [s, e) of chunk c of this wavefront
-    auto chunk_range = [&](int64_t c, int64_t& s, int64_t& e, int64_t& wi, int& kc) {
-        wi = gw + (c / a.nkc) * TW;
-        kc = (int)(c % a.nkc);
-        if (a.nkc == 1) {
-            s = wi * a.RW * a.rowB;
-            const int64_t rend = (wi + 1) * a.RW < a.M ? (wi + 1) * a.RW : a.M;
-            e = rend * a.rowB;
-        } else {
-            s = wi * a.rowB + (int64_t)kc * 64 * UB;
-            const int64_t lim = (wi + 1) * a.rowB;
-            e = s + 64 * UB < lim ? s + 64 * UB : lim;
-        }
-    };
-
-    uint4 pre[NJ];
-    auto load_chunk = [&](int64_t s, int64_t e) {
-        const int64_t s0 = s & ~(int64_t)15;
+    // Every argument is read once, up front, so the kernel-argument loads form
+    // one batch (no dependent scalar round trips before the first W load).
+    const int nseg = a.nseg, GU = a.GU, logP = a.logP, RW = a.RW, NKC = a.nkc;
+    const int64_t rowB = a.rowB, nwork = a.nwork;
+    const uint8_t* xq = a.xq;
+    const int G = a.G;
+    const uint8_t* sW[kMaxSeg];
+    float* sY[kMaxSeg];
+    int64_t sM[kMaxSeg], sW0[kMaxSeg];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int64_t off = s0 + 16 * (int64_t)(lane + 64 * j);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (off < e) {
-                if (off + 16 <= a.total) {
-                    v = *reinterpret_cast<const uint4*>(a.W + off);
-                } else {  // the last piece of W ends inside this 16-byte load
-                    uint32_t t[4] = {0, 0, 0, 0};
-                    for (int b = 0; b < 8 && off + 2 * b < a.total; ++b)
-                        t[b >> 1] |= (uint32_t)reinterpret_cast<const uint16_t*>(a.W + off)[b] << (16 * (b & 1));
-                    v = make_uint4(t[0], t[1], t[2], t[3]);
-                }
-            }
-            pre[j] = v;
+    for (int k = 0; k < kMaxSeg; ++k) {
+        sW[k] = a.seg[k].W;
+        sY[k] = a.seg[k].y;
+        sM[k] = a.seg[k].M;
+        sW0[k] = a.seg[k].work0;
+    }
+
+    const int lane = threadIdx.x & 63;
+    const int wpg = blockDim.x >> 6;
+    // wave-uniform bookkeeping lives in scalar registers
+    const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * wpg + (threadIdx.x >> 6)));
+    const int TW = gridDim.x * wpg;
+    const int P = 1 << logP;
+    // lane's place inside a chunk
+    const int lr = NKC == 1 ? lane >> logP : 0;
+    const int lg = NKC == 1 ? lane & (P - 1) : lane;
+    const bool lwriter = (lane & (P - 1)) == 0 && lr < RW;
+
+    // Where this lane's unit lies.
+    struct Loc {
+        const uint8_t* p;  // first byte of the unit (16-byte aligned), or null if none
+        float* y;          // output row base for this lane's row (lane 0 of the row writes)
+        int64_t ldy;       // stride between output columns (the segment's M)
+        int g;             // first 256-value activation group of the unit
+        bool last;         // last chunk of its work item
+        bool writer;
+    };
+    auto locate = [&](int64_t wi, int kc) {  // work item wi (uniform), chunk kc of it
+        Loc L;
+        const uint8_t* W = sW[0];
+        float* Y = sY[0];
+        int64_t M = sM[0], w0 = sW0[0];
+#pragma unroll
+        for (int k = 1; k < kMaxSeg; ++k) {
+            const bool in = k < nseg && wi >= sW0[k];
+            W = in ? sW[k] : W;
+            Y = in ? sY[k] : Y;
+            M = in ? sM[k] : M;
+            w0 = in ? sW0[k] : w0;
+        }
+        const int64_t row0 = (wi - w0) * RW;  // uniform
+        const int gu = kc * 64 + lg;  // kc is 0 when a row fits one chunk
+        const int64_t row = row0 + lr;
+        const bool valid = gu < GU && lr < RW && row < M;
+        L.p = valid ? W + row * rowB + (int64_t)gu * F::UB : nullptr;
+        L.y = Y + row;
+        L.ldy = M;
+        L.g = gu * (F::WPU / 256);
+        L.last = kc == NKC - 1;
+        L.writer = lwriter && row < M;
+        return L;
+    };
+    // Sub-step j of a unit: a window of NV 16-byte pieces.
+    auto load = [&](const Loc& L, int j, uint4 (&v)[NV]) {
+        if (L.p) {
+            const uint4* q = reinterpret_cast<const uint4*>(L.p + (SUB > 1 ? ((kQ6_KBytes * j) & ~15) : 0));
+#pragma unroll
+            for (int i = 0; i < NV; ++i) v[i] = q[i];
         }
     };
 
-    int64_t s, e, wi;
-    int kc;
-    chunk_range(0, s, e, wi, kc);
-    load_chunk(s, e);
+    uint4 buf[2][NV];
+    Loc cur, nxt;
+    int64_t nwi = gw;  // position of `nxt`: work item and chunk
+    int pkc = 0;
+    if (gw < nwork) nxt = locate(gw, 0);
+    stage_x<WT, NC>(xq, G, xl, [&]() {
+        if (gw < nwork) load(nxt, 0, buf[0]);
+    });
+    __syncthreads();
+    if (gw >= nwork) return;  // no barrier follows
 
     float acc[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) acc[n] = 0.f;
+    const int xstride = G * XREC;
 
-    for (int64_t c = 0; c < nch; ++c) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) reinterpret_cast<uint4*>(slot)[lane + 64 * j] = pre[j];
-        const int delta = (int)(s & 15);
-        const int64_t cw = wi;
-        const int ckc = kc;
-        if (c + 1 < nch) {
-            chunk_range(c + 1, s, e, wi, kc);
-            load_chunk(s, e);
+    // One sub-step: prefetch the next sub-step into the other buffer, then
+    // compute sub-step J of `cur` from buffer B.  J and B are compile-time.
+    auto step = [&](auto tag, bool more) {
+        constexpr int J = decltype(tag)::j, B = decltype(tag)::b;
+        if constexpr (J + 1 < SUB) load(cur, J + 1, buf[B ^ 1]);
+        else if (more) load(nxt, 0, buf[B ^ 1]);
+        if (cur.p) {
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(buf[B]);
+            const uint8_t* xr0 = xl + (cur.g + J) * XREC;
+            if constexpr (WT == QMM_Q4_0) unit_q4_0<NC>(w, xr0, xstride, acc);
+            else if constexpr (WT == QMM_Q8_0) unit_q8_0<NC>(w, xr0, xstride, acc);
+            else if constexpr (WT == QMM_Q4_K) unit_q4_k<NC>(w, xr0, xstride, acc);
+            else unit_q6_k<NC, 2 * J>(w, xr0, xstride, acc);  // super-block J starts 2J bytes into its window
         }
-        // this lane's unit inside the chunk
-        int r, g, uoff;
-        bool valid;
-        if (a.nkc == 1) {
-            r = lane >> a.logP;
-            g = lane & (P - 1);
-            valid = g < a.G && cw * a.RW + r < a.M && r < a.RW;
-            uoff = delta + (r * a.G + g) * UB;
-        } else {
-            r = 0;
-            g = ckc * 64 + lane;
-            valid = g < a.G;
-            uoff = delta + lane * UB;
-        }
-        if (valid) {
-            const uint8_t* xr0 = xl + g * XREC;
-            const int xstride = a.G * XREC;
-            const uint32_t* u = reinterpret_cast<const uint32_t*>(slot + uoff);
-            if constexpr (WT == QMM_Q4_0) unit_q4_0<NC>(u, xr0, xstride, acc);
-            else if constexpr (WT == QMM_Q8_0) unit_q8_0<NC>(u, xr0, xstride, acc);
-            else if constexpr (WT == QMM_Q4_K) unit_q4_k<NC>(u, xr0, xstride, acc);
-            else unit_q6_k<NC>(reinterpret_cast<const uint32_t*>(slot), uoff, xr0, xstride, acc);
-        }
-        if (ckc == a.nkc - 1) {
-            // butterfly over the P lanes of each row, then one lane stores
+    };
+    // After the last chunk of a work item: butterfly over the P lanes of
+    // each row, then one lane stores.
+    auto finish = [&]() {
+        if (cur.last) {
 #pragma unroll
             for (int n = 0; n < NC; ++n) {
                 float v = acc[n];
                 for (int o = P >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
-                acc[n] = v;
+                if (cur.writer) cur.y[n * cur.ldy] = v;
+                acc[n] = 0.f;
             }
-            const int64_t row = cw * a.RW + r;
-            if ((lane & (P - 1)) == 0 && r < a.RW && row < a.M) {
-#pragma unroll
-                for (int n = 0; n < NC; ++n) a.y[n * a.ldy + row] = acc[n];
-            }
-#pragma unroll
-            for (int n = 0; n < NC; ++n) acc[n] = 0.f;
+        }
+    };
+    auto advance = [&]() {  // make `nxt` current and locate the unit after it
+        cur = nxt;
+        if (++pkc == NKC) {
+            pkc = 0;
+            nwi += TW;
+        }
+        const bool more = nwi < nwork;
+        if (more) nxt = locate(nwi, pkc);
+        return more;
+    };
+
+    if constexpr (SUB == 1) {
+        for (;;) {
+            bool more = advance();
+            step(Tag<0, 0>{}, more);
+            finish();
+            if (!more) break;
+            more = advance();
+            step(Tag<0, 1>{}, more);
+            finish();
+            if (!more) break;
+        }
+    } else {
+        for (;;) {
+            const bool more = advance();
+            step(Tag<0, 0>{}, more);
+            step(Tag<1, 1>{}, more);
+            step(Tag<2, 0>{}, more);
+            step(Tag<3, 1>{}, more);
+            step(Tag<4, 0>{}, more);
+            step(Tag<5, 1>{}, more);
+            step(Tag<6, 0>{}, more);
+            step(Tag<7, 1>{}, more);
+            finish();
+            if (!more) break;
         }
     }
 }
 
-// ------------------------------------------- rows not a multiple of 256
-
-// Q4_0 / Q8_0 rows whose K is a multiple of 32 but not of 256: one wavefront
-// per row, lanes over the 32-value blocks, plain 2-byte loads.  Correct for
-// any such shape; the streaming kernel above handles the K % 256 == 0 case.
+// ------------------------------------------------ shapes the kernel above skips
+// Q4_0 / Q8_0 rows whose K is a multiple of 32 but not of 256, and Q6_K rows
+// whose K is not a multiple of 2048: one wavefront per row, lanes over the
+// blocks, plain 2-byte loads.  Correct for any such shape.
 template <int WT>
 __global__ __launch_bounds__(256) void gemv_rowwave_kernel(const uint8_t* __restrict__ W,
                                                            const uint8_t* __restrict__ xq, float* __restrict__ y,
                                                            int64_t M, int N, int64_t K) {
-    constexpr int WB = (WT == QMM_Q4_0) ? kQ4_0Bytes : kQ8_0Bytes;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= M) return;
-    const int64_t nb = K / 32;
-    for (int n = 0; n < N; ++n) {
-        float acc = 0.f;
-        for (int64_t b = lane; b < nb; b += 64) {
-            const uint8_t* wb = W + (row * nb + b) * WB;
-            const uint8_t* xb = xq + ((int64_t)n * nb + b) * kQ8_0Bytes;
-            const float dw = h2f(reinterpret_cast<const uint16_t*>(wb)[0]);
-            const float dx = h2f(reinterpret_cast<const uint16_t*>(xb)[0]);
-            int dot = 0;
-            if constexpr (WT == QMM_Q4_0) {
-                int sx = 0;
+    if constexpr (WT == QMM_Q4_0 || WT == QMM_Q8_0) {
+        constexpr int WB = (WT == QMM_Q4_0) ? kQ4_0Bytes : kQ8_0Bytes;
+        const int64_t nb = K / 32;
+        for (int n = 0; n < N; ++n) {
+            float acc = 0.f;
+            for (int64_t b = lane; b < nb; b += 64) {
+                const uint8_t* wb = W + (row * nb + b) * WB;
+                const uint8_t* xb = xq + ((int64_t)n * nb + b) * kQ8_0Bytes;
+                const float dw = h2f(reinterpret_cast<const uint16_t*>(wb)[0]);
+                const float dx = h2f(reinterpret_cast<const uint16_t*>(xb)[0]);
+                int dot = 0;
+                if constexpr (WT == QMM_Q4_0) {
+                    int sx = 0;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t q = ld_u16x2_g(wb + 2 + 4 * k);
-                    const uint32_t x0 = ld_u16x2_g(xb + 2 + 4 * k), x1 = ld_u16x2_g(xb + 18 + 4 * k);
-                    dot = dot4(q & 0x0F0F0F0Fu, x0, dot);
-                    dot = dot4((q >> 4) & 0x0F0F0F0Fu, x1, dot);
-                    sx = dot4(x0, 0x01010101u, sx);
-                    sx = dot4(x1, 0x01010101u, sx);
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t q = ld_u16x2_g(wb + 2 + 4 * k);
+                        const uint32_t x0 = ld_u16x2_g(xb + 2 + 4 * k), x1 = ld_u16x2_g(xb + 18 + 4 * k);
+                        dot = dot4(q & 0x0F0F0F0Fu, x0, dot);
+                        dot = dot4((q >> 4) & 0x0F0F0F0Fu, x1, dot);
+                        sx = dot4(x0, 0x01010101u, sx);
+                        sx = dot4(x1, 0x01010101u, sx);
+                    }
+                    dot -= 8 * sx;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        dot = dot4(ld_u16x2_g(wb + 2 + 4 * k), ld_u16x2_g(xb + 2 + 4 * k), dot);
                 }
-                dot -= 8 * sx;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) dot = dot4(ld_u16x2_g(wb + 2 + 4 * k), ld_u16x2_g(xb + 2 + 4 * k), dot);
+                acc += (float)dot * (dw * dx);
             }
-            acc += (float)dot * (dw * dx);
-        }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-        if (lane == 0) y[(int64_t)n * M + row] = acc;
+            for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+            if (lane == 0) y[(int64_t)n * M + row] = acc;
+        }
+    } else {  // Q6_K x Q8_K, one super-block per lane step
+        const int64_t nb = K / 256;
+        for (int n = 0; n < N; ++n) {
+            float acc = 0.f;
+            for (int64_t b = lane; b < nb; b += 64) {
+                const uint8_t* wb = W + (row * nb + b) * kQ6_KBytes;
+                const uint8_t* xb = xq + ((int64_t)n * nb + b) * kQ8_KBytes;
+                int isum = 0;
+                for (int j = 0; j < 16; ++j) {
+                    const int sc = (int8_t)wb[192 + j];
+                    const int h = j >> 3, c = (j >> 1) & 3, kk = j & 1;
+                    int t = 0;
+                    for (int k4 = 0; k4 < 4; ++k4) {
+                        const int l = 16 * kk + 4 * k4;
+                        uint32_t qlw = ld_u16x2_g(wb + 64 * h + 32 * (c & 1) + l);
+                        const uint32_t lo = (c < 2) ? (qlw & 0x0F0F0F0Fu) : ((qlw >> 4) & 0x0F0F0F0Fu);
+                        const uint32_t hi = (ld_u16x2_g(wb + 128 + 32 * h + l) >> (2 * c)) & 0x03030303u;
+                        t = dot4(lo | (hi << 4), reinterpret_cast<const uint32_t*>(xb + 4)[4 * j + k4], t);
+                    }
+                    isum += sc * (t - 32 * (int)reinterpret_cast<const int16_t*>(xb + 260)[j]);
+                }
+                const float dw = h2f(reinterpret_cast<const uint16_t*>(wb + 208)[0]);
+                acc += (dw * reinterpret_cast<const float*>(xb)[0]) * (float)isum;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+            if (lane == 0) y[(int64_t)n * M + row] = acc;
+        }
     }
 }
 
@@ -467,102 +588,121 @@ DevInfo& dev_info() {
         }
         if (d.cus <= 0) d.cus = 256;
         if (d.lds < 65536) d.lds = 65536;
+        if (d.lds > 160 * 1024) d.lds = 160 * 1024;
     }
     return d;
 }
 
-template <int WT, int NC, int WAVES>
-hipError_t launch_one(const GemvArgs& a, size_t lds, int grid, hipStream_t s) {
-    static bool attr_set = false;  // raising the LDS limit is idempotent
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<WT, NC, WAVES>),
+template <int WT, int NC>
+hipError_t launch_one(const GemvArgs& a, size_t lds, int wpg, hipStream_t s) {
+    static int occ[9] = {0};  // workgroups per CU, by waves per workgroup
+    if (!occ[wpg]) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<WT, NC>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set = true;
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<WT, NC>, wpg * 64, lds) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        occ[wpg] = n;
     }
-    hipLaunchKernelGGL((gemv_kernel<WT, NC, WAVES>), dim3(grid), dim3(WAVES * 64), lds, s, a);
+    const DevInfo& di = dev_info();
+    const int per_cu = (int)(di.lds / (lds ? lds : 1)) < occ[wpg] ? (int)(di.lds / (lds ? lds : 1)) : occ[wpg];
+    const int64_t need = (a.nwork + wpg - 1) / wpg;
+    const int64_t cap = (int64_t)di.cus * (per_cu > 0 ? per_cu : 1);
+    const int grid = (int)(need < cap ? need : cap);
+    hipLaunchKernelGGL((gemv_kernel<WT, NC>), dim3(grid), dim3(wpg * 64), lds, s, a);
     return hipGetLastError();
 }
 
-template <int WT, int WAVES>
-hipError_t dispatch_nc(int nc, const GemvArgs& a, size_t lds, int grid, hipStream_t s) {
+template <int WT>
+hipError_t dispatch_nc(int nc, const GemvArgs& a, size_t lds, int wpg, hipStream_t s) {
     switch (nc) {
-    case 1: return launch_one<WT, 1, WAVES>(a, lds, grid, s);
-    case 2: return launch_one<WT, 2, WAVES>(a, lds, grid, s);
-    case 3: return launch_one<WT, 3, WAVES>(a, lds, grid, s);
-    case 4: return launch_one<WT, 4, WAVES>(a, lds, grid, s);
-    case 5: return launch_one<WT, 5, WAVES>(a, lds, grid, s);
-    case 6: return launch_one<WT, 6, WAVES>(a, lds, grid, s);
-    case 7: return launch_one<WT, 7, WAVES>(a, lds, grid, s);
-    case 8: return launch_one<WT, 8, WAVES>(a, lds, grid, s);
+    case 1: return launch_one<WT, 1>(a, lds, wpg, s);
+    case 2: return launch_one<WT, 2>(a, lds, wpg, s);
+    case 3: return launch_one<WT, 3>(a, lds, wpg, s);
+    case 4: return launch_one<WT, 4>(a, lds, wpg, s);
+    case 5: return launch_one<WT, 5>(a, lds, wpg, s);
+    case 6: return launch_one<WT, 6>(a, lds, wpg, s);
+    case 7: return launch_one<WT, 7>(a, lds, wpg, s);
+    case 8: return launch_one<WT, 8>(a, lds, wpg, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int WT>
-hipError_t gemv_typed(const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-    using F = GFmt<WT>;
+hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const int64_t* Ms, const void* xq,
+                      int64_t N, int64_t K, hipStream_t s) {
+    using F = U<WT>;
     const DevInfo& di = dev_info();
-    const size_t lds_cap = di.lds < 160 * 1024 ? di.lds : 160 * 1024;
-    const int G = (int)(K / 256);
-    const int64_t xrowB = (int64_t)G * (WT == QMM_Q4_0 || WT == QMM_Q8_0 ? 8 * kQ8_0Bytes : kQ8_KBytes);
     GemvArgs a;
-    a.W = static_cast<const uint8_t*>(W);
-    a.M = M;
-    a.rowB = (int64_t)G * F::UB;
-    a.total = M * a.rowB;
-    a.ldy = M;
-    a.G = G;
-    const int Pl = G >= 64 ? 64 : G;
+    a.nseg = nseg;
+    a.G = (int)(K / 256);
+    a.GU = (int)(K / F::WPU);
+    a.rowB = (int64_t)a.GU * F::UB;
+    const int Pl = a.GU >= 64 ? 64 : a.GU;
     int logP = 0;
     while ((1 << logP) < Pl) ++logP;
     a.logP = logP;
-    a.RW = G >= 64 ? 1 : 64 >> logP;
-    a.nkc = (G + 63) / 64;
-    a.nwork = (M + a.RW - 1) / a.RW;
-    const size_t slot = (size_t)F::NJ * 1024;
+    a.RW = a.GU >= 64 ? 1 : 64 >> logP;
+    a.nkc = (a.GU + 63) / 64;
+    int64_t work = 0;
+    for (int i = 0; i < nseg; ++i) {
+        a.seg[i].W = static_cast<const uint8_t*>(Ws[i]);
+        a.seg[i].M = Ms[i];
+        a.seg[i].work0 = work;
+        work += (Ms[i] + a.RW - 1) / a.RW;
+    }
+    for (int i = nseg; i < kMaxSeg; ++i) a.seg[i] = a.seg[0];
+    a.nwork = work;
+    const int64_t xrowB = (int64_t)a.G * (WT == QMM_Q4_0 || WT == QMM_Q8_0 ? 8 * kQ8_0Bytes : kQ8_KBytes);
+    // waves per workgroup: spread small problems over all CUs
+    const int64_t per_cu = (work + di.cus - 1) / di.cus;
+    const int wpg = per_cu >= 8 ? 8 : per_cu >= 4 ? 4 : per_cu >= 2 ? 2 : 1;
     for (int64_t n0 = 0; n0 < N;) {
-        // columns per launch: as many (<= 8) as leave room for >= 2 wavefronts' slots
         int nc = (int)(N - n0 < 8 ? N - n0 : 8);
-        while (nc > 1 && (size_t)nc * G * XREC + 2 * slot > lds_cap) --nc;
-        const size_t xbytes = (size_t)nc * G * XREC;
-        if (xbytes + 2 * slot > lds_cap) return hipErrorInvalidValue;
-        int waves = 8;
-        while (waves > 2 && xbytes + waves * slot > lds_cap) waves >>= 1;
-        const size_t lds = xbytes + waves * slot;
-        const int per_cu = (int)(lds_cap / lds) > 0 ? (int)(lds_cap / lds) : 1;
-        const int64_t need = (a.nwork + waves - 1) / waves;
-        const int64_t cap = (int64_t)di.cus * (per_cu < 2 ? per_cu : 2);
-        const int grid = (int)(need < cap ? need : cap);
+        while (nc > 1 && (size_t)nc * a.G * XREC > di.lds) --nc;
+        const size_t lds = (size_t)nc * a.G * XREC;
+        if (lds > di.lds) return hipErrorInvalidValue;
         a.xq = static_cast<const uint8_t*>(xq) + n0 * xrowB;
-        a.y = y + n0 * M;
-        hipError_t err;
-        if (waves == 8) err = dispatch_nc<WT, 8>(nc, a, lds, grid, s);
-        else if (waves == 4) err = dispatch_nc<WT, 4>(nc, a, lds, grid, s);
-        else err = dispatch_nc<WT, 2>(nc, a, lds, grid, s);
+        for (int i = 0; i < nseg; ++i) a.seg[i].y = ys[i] + n0 * Ms[i];
+        for (int i = nseg; i < kMaxSeg; ++i) a.seg[i].y = a.seg[0].y;
+        hipError_t err = dispatch_nc<WT>(nc, a, lds, wpg, s);
         if (err != hipSuccess) return err;
         n0 += nc;
     }
     return hipSuccess;
 }
 
+hipError_t rowwave(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+                   hipStream_t s) {
+    const dim3 g((unsigned)((M + 3) / 4)), b(256);
+    const uint8_t* w = static_cast<const uint8_t*>(W);
+    const uint8_t* x = static_cast<const uint8_t*>(xq);
+    if (wtype == QMM_Q4_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q4_0>, g, b, 0, s, w, x, y, M, (int)N, K);
+    else if (wtype == QMM_Q8_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q8_0>, g, b, 0, s, w, x, y, M, (int)N, K);
+    else if (wtype == QMM_Q6_K) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q6_K>, g, b, 0, s, w, x, y, M, (int)N, K);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+bool needs_rowwave(int wtype, int64_t K) {
+    if (wtype == QMM_Q6_K) return K % 2048 != 0;
+    return K % 256 != 0;
+}
+
 }  // namespace
 
 hipError_t launch_gemv(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
-    if (K % 256 != 0) {
-        const dim3 g((unsigned)((M + 3) / 4)), b(256);
-        const uint8_t* w = static_cast<const uint8_t*>(W);
-        const uint8_t* x = static_cast<const uint8_t*>(xq);
-        if (wtype == QMM_Q4_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q4_0>, g, b, 0, s, w, x, y, M, (int)N, K);
-        else if (wtype == QMM_Q8_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q8_0>, g, b, 0, s, w, x, y, M, (int)N, K);
-        else return hipErrorInvalidValue;
-        return hipGetLastError();
-    }
+    if (needs_rowwave(wtype, K)) return rowwave(wtype, W, xq, y, M, N, K, s);
+    const void* Ws[1] = {W};
+    float* ys[1] = {y};
+    const int64_t Ms[1] = {M};
     switch (wtype) {
-    case QMM_Q4_0: return gemv_typed<QMM_Q4_0>(W, xq, y, M, N, K, s);
-    case QMM_Q8_0: return gemv_typed<QMM_Q8_0>(W, xq, y, M, N, K, s);
-    case QMM_Q4_K: return gemv_typed<QMM_Q4_K>(W, xq, y, M, N, K, s);
-    case QMM_Q6_K: return gemv_typed<QMM_Q6_K>(W, xq, y, M, N, K, s);
+    case QMM_Q4_0: return gemv_typed<QMM_Q4_0>(1, Ws, ys, Ms, xq, N, K, s);
+    case QMM_Q8_0: return gemv_typed<QMM_Q8_0>(1, Ws, ys, Ms, xq, N, K, s);
+    case QMM_Q4_K: return gemv_typed<QMM_Q4_K>(1, Ws, ys, Ms, xq, N, K, s);
+    case QMM_Q6_K: return gemv_typed<QMM_Q6_K>(1, Ws, ys, Ms, xq, N, K, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -115,7 +115,8 @@ def test_config_q6_k_head(N):
 def test_small_and_ragged_shapes(wt):
     g = np.random.default_rng(50 + wt)
     shapes = [(1, 1, 256), (7, 3, 256), (33, 8, 512), (100, 2, 1024), (257, 5, 768),
-              (65, 1, 16384), (9, 2, 16640), (3, 1, 33024), (130, 4, 2304)]
+              (65, 1, 16384), (9, 2, 16640), (3, 1, 33024), (130, 4, 2304),
+              (65, 3, 6144), (300, 1, 4096), (4, 8, 14336)]
     if wt in (Q.QMM_Q4_0, Q.QMM_Q8_0):
         shapes += [(5, 2, 32), (17, 1, 96), (64, 3, 288), (3, 8, 2080)]
     for M, N, K in shapes:
