@@ -3,17 +3,19 @@
 
 Headline (`value`): GEMV effective GB/s at batch 1 on the Q4_0 x Q8_0 decode
 workload with 1B-Llama layer shapes: one step is one decode token's worth of
-the hot path through 16 layers, each layer
-    quantize x (K=2048) -> GEMV attn_q 2048x2048, attn_k 512x2048, attn_v 512x2048
-    quantize x (K=2048) -> GEMV attn_output 2048x2048
-    quantize x (K=2048) -> GEMV ffn_gate 8192x2048, ffn_up 8192x2048
-    quantize x (K=8192) -> GEMV ffn_down 2048x8192
-(the quantizes stand where the model's activations change; what runs between
-them in a model - attention, norms, SwiGLU - is outside this library).  The
-step is captured once in a HIP graph and replayed.  547 MB of weights per step
-exceed the 256 MB Infinity Cache, so every step streams W from HBM.
-Bytes are algorithmic: W blocks + quantized activations + fp32 outputs of
-every GEMV, plus fp32 in / blocks out of every quantize.
+the hot path through 16 layers, each layer four dependent launches, each of
+which quantizes its fp32 activation row to Q8_0 and multiplies:
+    x (K=2048) -> attn_q 2048x2048 | attn_k 512x2048 | attn_v 512x2048
+    x (K=2048) -> attn_output 2048x2048
+    x (K=2048) -> ffn_gate 8192x2048 | ffn_up 8192x2048
+    x (K=8192) -> ffn_down 2048x8192
+(the four inputs stand where the model's activations change; what runs
+between them in a model - attention, norms, SwiGLU - is outside this
+library).  The step is captured once in a HIP graph and replayed.  547 MB of
+weights per step exceed the 256 MB Infinity Cache, so every step streams W
+from HBM.  Bytes are algorithmic: W blocks + fp32 activation rows + fp32
+outputs.  The same work with separate quantize launches and one launch per
+matrix (176 launches) is reported beside it.
 
 Also reported: the int8 GEMM rate at batch 512 (Q4_K 4096x4096 and 14336x4096
 prefill), the other GEMV workloads, the dominant kernel's roofline from HIP
@@ -103,6 +105,10 @@ class Bench:
 # ---------------------------------------------------------------- headline
 
 def decode_sweep(b: Bench, steps: int, warmup: int, keep_cpu_layers: int):
+    """The 16-layer 1B-shaped Q4_0 decode step.  Fused form (the value): one
+    qmm_mul_mat_multi launch per stage, quantizing its fp32 input itself:
+    q|k|v, o, gate|up, down.  Unfused form (reported beside it): a
+    qmm_quantize_act launch per stage, then one qmm_mul_mat per matrix."""
     import synth
     torch, Q = b.torch, b.Q
     g = synth.rng(0)
@@ -130,57 +136,57 @@ def decode_sweep(b: Bench, steps: int, warmup: int, keep_cpu_layers: int):
 
     stages = (("attn", ("attn_q", "attn_k", "attn_v")), ("o", ("attn_output",)),
               ("ffn", ("ffn_gate", "ffn_up")), ("down", ("ffn_down",)))
-    gemv_calls, quant_calls = [], []
+    import ctypes
+    launches = []  # (x fp32 ptr, K, [(W ptr, y ptr, M)])
     for li, L in enumerate(layers):
         for xname, mats in stages:
             x = xs[li][xname]
-            K = x.shape[1]
-            quant_calls.append((x.data_ptr(), xq[K].data_ptr(), K))
-            for m in mats:
-                blocks, M, KK = L[m]
-                gemv_calls.append((blocks.data_ptr(), xq[K].data_ptr(), ys[m].data_ptr(), M, KK, len(quant_calls) - 1))
-
+            launches.append((x.data_ptr(), x.shape[1],
+                             [(L[m][0].data_ptr(), ys[m].data_ptr(), L[m][1]) for m in mats]))
+    packed = []
+    for xp, K, mats in launches:
+        n = len(mats)
+        packed.append((xp, K, n, (ctypes.c_void_p * n)(*[m[0] for m in mats]),
+                       (ctypes.c_void_p * n)(*[m[1] for m in mats]), (ctypes.c_int64 * n)(*[m[2] for m in mats])))
     lib = Q.lib()
 
-    def step():
+    def step_fused():
         s = torch.cuda.current_stream().cuda_stream
-        qi = 0
-        for (w, xp, yp, M, K, qidx) in gemv_calls:
-            while qi <= qidx:
-                x, o, KK = quant_calls[qi]
-                rc = lib.qmm_quantize_act(Q.QMM_Q8_0, x, o, 1, KK, s)
-                if rc:
-                    raise RuntimeError(Q.qmm_strerror(rc))
-                qi += 1
-            rc = lib.qmm_mul_mat(Q.QMM_Q4_0, w, xp, yp, M, 1, K, s)
+        for xp, K, n, Wa, ya, Ma in packed:
+            rc = lib.qmm_mul_mat_multi(Q.QMM_Q4_0, n, Wa, ya, Ma, xp, 1, 1, K, s)
             if rc:
                 raise RuntimeError(Q.qmm_strerror(rc))
 
-    def gemv_only():
+    def step_unfused():
         s = torch.cuda.current_stream().cuda_stream
-        for (w, xp, yp, M, K, _) in gemv_calls:
-            lib.qmm_mul_mat(Q.QMM_Q4_0, w, xp, yp, M, 1, K, s)
+        for xp, K, mats in launches:
+            rc = lib.qmm_quantize_act(Q.QMM_Q8_0, xp, xq[K].data_ptr(), 1, K, s)
+            if rc:
+                raise RuntimeError(Q.qmm_strerror(rc))
+            for w, y, M in mats:
+                rc = lib.qmm_mul_mat(Q.QMM_Q4_0, w, xq[K].data_ptr(), y, M, 1, K, s)
+                if rc:
+                    raise RuntimeError(Q.qmm_strerror(rc))
 
-    def gemv_bytes(M, K):
-        return M * (K // 32) * 18 + (K // 32) * 34 + 4 * M
+    w_bytes = sum(M * (K // 32) * 18 for _, K, mats in launches for (_, _, M) in mats)
+    y_bytes = sum(4 * M for _, K, mats in launches for (_, _, M) in mats)
+    # fused: each launch reads its fp32 row once; unfused: quantize reads fp32
+    # and writes blocks, each GEMV reads the blocks
+    bytes_fused = w_bytes + y_bytes + sum(4 * K for _, K, _ in launches)
+    bytes_unfused = w_bytes + y_bytes + sum(4 * K + (K // 32) * 34 * (1 + len(m)) for _, K, m in launches)
 
-    bytes_gemv = sum(gemv_bytes(M, K) for (_, _, _, M, K, _) in gemv_calls)
-    bytes_quant = sum(4 * K + (K // 32) * 34 for (_, _, K) in quant_calls)
-    bytes_step = bytes_gemv + bytes_quant
-    w_bytes = sum(M * (K // 32) * 18 for (_, _, _, M, K, _) in gemv_calls)
-
-    g_step = b.graph(step)
-    sec = b.time_graph(g_step, steps, warmup)
-    g_gemv = b.graph(gemv_only)
-    sec_gemv = b.time_graph(g_gemv, steps, warmup)
-    res = {
-        "bytes_step": bytes_step, "w_bytes": w_bytes, "seconds": sec, "steps": steps,
-        "gbs": bytes_step * steps / sec / 1e9, "ms_per_step": sec / steps * 1e3,
-        "gemv_launches_per_step": len(gemv_calls), "quantize_launches_per_step": len(quant_calls),
-        "gemv_bytes_per_step": bytes_gemv, "gemv_seconds": sec_gemv,
-        "gemv_gbs": bytes_gemv * steps / sec_gemv / 1e9,
-    }
-    return res, cpu_f32
+    g_fused = b.graph(step_fused)
+    sec = b.time_graph(g_fused, steps, warmup)
+    g_unf = b.graph(step_unfused)
+    sec_unf = b.time_graph(g_unf, steps, warmup)
+    return {
+        "bytes_step": bytes_fused, "w_bytes": w_bytes, "seconds": sec, "steps": steps,
+        "gbs": bytes_fused * steps / sec / 1e9, "ms_per_step": sec / steps * 1e3,
+        "launches_per_step": len(launches),
+        "unfused": {"gbs": round(bytes_unfused * steps / sec_unf / 1e9, 2),
+                    "ms_per_step": round(sec_unf / steps * 1e3, 4),
+                    "launches_per_step": len(launches) + sum(len(m) for _, _, m in launches)},
+    }, cpu_f32
 
 
 def cpu_baseline_decode(cpu_f32, min_seconds=10.0):
@@ -280,7 +286,7 @@ def main():
         sys.exit(2)
     b = Bench()
     head, cpu_f32 = decode_sweep(b, a.steps, a.warmup, keep_cpu_layers=0 if a.no_cpu else 2)
-    gemv_us = head["gemv_seconds"] / (a.steps * head["gemv_launches_per_step"]) * 1e6
+    gemv_us = head["seconds"] / (a.steps * head["launches_per_step"]) * 1e6
     line = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -297,22 +303,24 @@ def main():
         "config": {
             "workload": "Q4_0 x Q8_0 decode GEMV, batch 1, 1B-Llama layer shapes (attn_q/attn_output "
                         "2048x2048, attn_k/attn_v 512x2048, ffn_gate/ffn_up 8192x2048, ffn_down 2048x8192) "
-                        "x 16 layers, W ~ N(0,0.02) quantized to Q4_0, x ~ N(0,1) quantized to Q8_0, seed 0",
+                        "x 16 layers, W ~ N(0,0.02) quantized to Q4_0, x ~ N(0,1) quantized to Q8_0 inside "
+                        "each launch (q|k|v, o, gate|up, down: 4 launches per layer), seed 0",
             "bytes_per_step": head["bytes_step"],
             "weight_bytes_per_step": head["w_bytes"],
-            "launches_per_step": head["gemv_launches_per_step"] + head["quantize_launches_per_step"],
+            "launches_per_step": head["launches_per_step"],
             "frac_hbm_peak": round(head["gbs"] / HBM_PEAK_GBS, 4),
+            "unfused_same_work": head["unfused"],
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel<Q4_0, 1 column>",
-            "achieved": round(head["gemv_gbs"], 2),
+            "kernel": "gemv_kernel<Q4_0, 1 column, fused quantize>",
+            "achieved": round(head["gbs"], 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(head["gemv_gbs"] / HBM_PEAK_GBS, 4),
+            "frac": round(head["gbs"] / HBM_PEAK_GBS, 4),
             "traffic": None,
             "avg_launch_us": round(gemv_us, 3),
-            "launches": head["gemv_launches_per_step"] * a.steps,
+            "launches": head["launches_per_step"] * a.steps,
         },
     }
     if not a.quick:

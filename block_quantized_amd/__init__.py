@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
             "qmm_dequantize": (I, [I, P, P, I64, I64, P]),
             "qmm_mul_mat": (I, [I, P, P, P, I64, I64, I64, P]),
             "qmm_mul_mat_algo": (I, [I, P, P, P, I64, I64, I64, I, P]),
+            "qmm_mul_mat_multi": (I, [I, I, P, P, P, P, I, I64, I64, P]),
             "qmm_strerror": (ctypes.c_char_p, [I]),
         }
         for name, (res, args) in sig.items():
@@ -62,7 +63,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("qmm_block_size", "qmm_block_bytes", "qmm_row_bytes", "qmm_vec_dot_type", "qmm_quantize_act",
-            "qmm_quantize", "qmm_dequantize", "qmm_mul_mat", "qmm_mul_mat_algo", "qmm_strerror")
+            "qmm_quantize", "qmm_dequantize", "qmm_mul_mat", "qmm_mul_mat_algo", "qmm_mul_mat_multi",
+            "qmm_strerror")
 
 
 def _ptr(a):
@@ -120,6 +122,14 @@ def qmm_mul_mat_algo(wtype, W, xq, y, M, N, K, algo, stream=None) -> int:
     return lib().qmm_mul_mat_algo(wtype, _ptr(W), _ptr(xq), _ptr(y), M, N, K, algo, _stream(stream))
 
 
+def qmm_mul_mat_multi(wtype, count, W, y, M, x, x_is_f32, N, K, stream=None) -> int:
+    """W, y: sequences of `count` device buffers (tensors or addresses); M: row counts."""
+    Wa = (ctypes.c_void_p * max(count, 1))(*[_ptr(w) for w in W[:count]]) if W is not None else None
+    ya = (ctypes.c_void_p * max(count, 1))(*[_ptr(t) for t in y[:count]]) if y is not None else None
+    Ma = (ctypes.c_int64 * max(count, 1))(*M[:count]) if M is not None else None
+    return lib().qmm_mul_mat_multi(wtype, count, Wa, ya, Ma, _ptr(x), int(bool(x_is_f32)), N, K, _stream(stream))
+
+
 def qmm_strerror(code: int) -> str:
     return lib().qmm_strerror(code).decode()
 
@@ -153,6 +163,14 @@ def dequantize(t: int, blocks, rows: int, K: int, stream=None):
     out = torch.empty((rows, K), dtype=torch.float32, device=blocks.device)
     _check(qmm_dequantize(t, blocks, out, rows, K, stream), "qmm_dequantize")
     return out
+
+
+def mul_mat_multi(wtype: int, Ws, Ms, x, N: int, K: int, x_is_f32: bool = False, stream=None):
+    """Several matrices sharing x in one launch -> list of (N, M_i) outputs."""
+    import torch
+    ys = [torch.empty((N, M), dtype=torch.float32, device=x.device) for M in Ms]
+    _check(qmm_mul_mat_multi(wtype, len(Ws), Ws, ys, list(Ms), x, x_is_f32, N, K, stream), "qmm_mul_mat_multi")
+    return ys
 
 
 def mul_mat(wtype: int, W, xq, M: int, N: int, K: int, algo: int = 0, stream=None):

@@ -19,16 +19,6 @@
 namespace qmm {
 namespace {
 
-// roundf(t) as an int8 code: NaN (0 * Inf when 1/d overflowed) -> 0, then
-// clamp to [-127, 127].
-__device__ __forceinline__ int rtn_code(float t) {
-    float r = roundf(t);
-    if (r != r) return 0;
-    if (r > 127.0f) return 127;
-    if (r < -127.0f) return -127;
-    return (int)r;
-}
-
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
     return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
            ((uint32_t)(d & 0xFF) << 24);
@@ -62,8 +52,8 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
     a = fmaxf(a, __shfl_xor(a, 2));
     a = fmaxf(a, __shfl_xor(a, 4));
     if (b >= nblocks) return;
-    const float d = a / 127.0f;
-    const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    float d, id;
+    rtn_scale(a, d, id);
     const uint32_t q = pack4(rtn_code(v.x * id), rtn_code(v.y * id), rtn_code(v.z * id), rtn_code(v.w * id));
     uint8_t* blk = out + b * kQ8_0Bytes;
     st_u16x2(blk + 2 + 4 * sub, q);
@@ -83,8 +73,8 @@ __global__ __launch_bounds__(256) void quantize_q8_k_kernel(const float* __restr
     float a = amax4(v);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) a = fmaxf(a, __shfl_xor(a, m));
-    const float d = a / 127.0f;
-    const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    float d, id;
+    rtn_scale(a, d, id);
     const int q0 = rtn_code(v.x * id), q1 = rtn_code(v.y * id), q2 = rtn_code(v.z * id), q3 = rtn_code(v.w * id);
     int s = q0 + q1 + q2 + q3;
     s += __shfl_xor(s, 1);

@@ -89,14 +89,97 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
 // for x - loads retire in order - does not wait for W).  The activation rows
 // are contiguous, so item i's bytes follow item i-1's.
 
-template <int WT, int NC, class Hook>
+template <int WT, int NC, bool XF, class Hook>
 __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, Hook&& after_loads) {
     constexpr bool kQ80 = (WT == QMM_Q4_0 || WT == QMM_Q8_0);
-    constexpr int KB = 4;  // items per thread per round
+    constexpr int KB = XF ? 1 : 4;  // items per thread per round
     const int nitems = kQ80 ? NC * G * 8 : NC * G * 4;
     const int step = KB * blockDim.x;
     for (int base = 0, round = 0; base < nitems || round == 0; base += step, ++round) {
-        if constexpr (kQ80) {
+        if constexpr (XF && kQ80) {
+            // fp32 rows quantized here to Q8_0, exactly as the stand-alone
+            // quantizer does: item i = values 32i .. 32i+31.
+            const int i = base + threadIdx.x;
+            float4 v[8];
+            if (i < nitems) {
+#pragma unroll
+                for (int h = 0; h < 8; ++h) v[h] = reinterpret_cast<const float4*>(xq)[8 * i + h];
+            }
+            if (round == 0) after_loads();
+            if (i < nitems) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int h = 0; h < 8; ++h)
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[h].x), fabsf(v[h].y)), fmaxf(fabsf(v[h].z), fabsf(v[h].w))));
+                float d, id;
+                rtn_scale(amax, d, id);
+                uint32_t q[8];
+                int sx = 0;
+#pragma unroll
+                for (int h = 0; h < 8; ++h) {
+                    q[h] = (uint32_t)(rtn_code(v[h].x * id) & 0xFF) | ((uint32_t)(rtn_code(v[h].y * id) & 0xFF) << 8) |
+                           ((uint32_t)(rtn_code(v[h].z * id) & 0xFF) << 16) |
+                           ((uint32_t)(rtn_code(v[h].w * id) & 0xFF) << 24);
+                    sx = dot4(q[h], 0x01010101u, sx);
+                }
+                uint8_t* rec = xl + (i >> 3) * XREC;
+                const int bi = i & 7;
+                reinterpret_cast<uint4*>(rec + 32 * bi)[0] = make_uint4(q[0], q[1], q[2], q[3]);
+                reinterpret_cast<uint4*>(rec + 32 * bi)[1] = make_uint4(q[4], q[5], q[6], q[7]);
+                reinterpret_cast<float*>(rec)[64 + bi] = h2f(f2h(d));  // the block stores fp16(d)
+                reinterpret_cast<int*>(rec)[72 + bi] = 8 * sx;
+            }
+        } else if constexpr (XF) {
+            // fp32 rows quantized here to Q8_K: item i = quarter i&3 of block
+            // i>>2 (values 64i .. 64i+63); the four quarters of a block are
+            // adjacent lanes and share the block maximum through shuffles.
+            const int i = base + threadIdx.x;
+            float4 v[16];
+            float amax = 0.0f;
+            if (i < nitems) {
+#pragma unroll
+                for (int h = 0; h < 16; ++h) v[h] = reinterpret_cast<const float4*>(xq)[16 * i + h];
+            }
+            if (round == 0) after_loads();
+            if (i < nitems) {
+#pragma unroll
+                for (int h = 0; h < 16; ++h)
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[h].x), fabsf(v[h].y)), fmaxf(fabsf(v[h].z), fabsf(v[h].w))));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            if (i < nitems) {
+                float d, id;
+                rtn_scale(amax, d, id);
+                uint8_t* rec = xl + (i >> 2) * XREC;
+                const int qq = i & 3;
+                int bs[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    uint32_t q[4];
+                    int sum = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float4 f = v[4 * t + u];
+                        q[u] = (uint32_t)(rtn_code(f.x * id) & 0xFF) | ((uint32_t)(rtn_code(f.y * id) & 0xFF) << 8) |
+                               ((uint32_t)(rtn_code(f.z * id) & 0xFF) << 16) |
+                               ((uint32_t)(rtn_code(f.w * id) & 0xFF) << 24);
+                        sum = dot4(q[u], 0x01010101u, sum);
+                    }
+                    bs[t] = sum;  // exact sum of codes 64qq+16t .. +15
+                    reinterpret_cast<uint4*>(rec + 64 * qq)[t] = make_uint4(q[0], q[1], q[2], q[3]);
+                }
+                int* meta = reinterpret_cast<int*>(rec) + 65;
+                if constexpr (WT == QMM_Q4_K) {
+                    meta[2 * qq] = bs[0] + bs[1];
+                    meta[2 * qq + 1] = bs[2] + bs[3];
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) meta[4 * qq + t] = 32 * bs[t];
+                }
+                if (qq == 0) reinterpret_cast<float*>(rec)[64] = d;
+            }
+        } else if constexpr (kQ80) {
             uint32_t v[KB][17];
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
@@ -332,7 +415,7 @@ __device__ __forceinline__ void unit_q6_k(const uint32_t* r, const uint8_t* xr0,
 
 // ------------------------------------------------------------- kernel
 
-template <int WT, int NC>
+template <int WT, int NC, bool XF>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     using F = U<WT>;
     constexpr int NV = F::NV, SUB = F::SUB;
@@ -414,7 +497,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     int64_t nwi = gw;  // position of `nxt`: work item and chunk
     int pkc = 0;
     if (gw < nwork) nxt = locate(gw, 0);
-    stage_x<WT, NC>(xq, G, xl, [&]() {
+    stage_x<WT, NC, XF>(xq, G, xl, [&]() {
         if (gw < nwork) load(nxt, 0, buf[0]);
     });
     __syncthreads();
@@ -593,14 +676,15 @@ DevInfo& dev_info() {
     return d;
 }
 
-template <int WT, int NC>
+template <int WT, int NC, bool XF>
 hipError_t launch_one(const GemvArgs& a, size_t lds, int wpg, hipStream_t s) {
     static int occ[9] = {0};  // workgroups per CU, by waves per workgroup
     if (!occ[wpg]) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<WT, NC>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<WT, NC, XF>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<WT, NC>, wpg * 64, lds) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<WT, NC, XF>, wpg * 64, lds) !=
+                hipSuccess ||
             n <= 0)
             n = 1;
         occ[wpg] = n;
@@ -610,28 +694,28 @@ hipError_t launch_one(const GemvArgs& a, size_t lds, int wpg, hipStream_t s) {
     const int64_t need = (a.nwork + wpg - 1) / wpg;
     const int64_t cap = (int64_t)di.cus * (per_cu > 0 ? per_cu : 1);
     const int grid = (int)(need < cap ? need : cap);
-    hipLaunchKernelGGL((gemv_kernel<WT, NC>), dim3(grid), dim3(wpg * 64), lds, s, a);
+    hipLaunchKernelGGL((gemv_kernel<WT, NC, XF>), dim3(grid), dim3(wpg * 64), lds, s, a);
     return hipGetLastError();
 }
 
-template <int WT>
+template <int WT, bool XF>
 hipError_t dispatch_nc(int nc, const GemvArgs& a, size_t lds, int wpg, hipStream_t s) {
     switch (nc) {
-    case 1: return launch_one<WT, 1>(a, lds, wpg, s);
-    case 2: return launch_one<WT, 2>(a, lds, wpg, s);
-    case 3: return launch_one<WT, 3>(a, lds, wpg, s);
-    case 4: return launch_one<WT, 4>(a, lds, wpg, s);
-    case 5: return launch_one<WT, 5>(a, lds, wpg, s);
-    case 6: return launch_one<WT, 6>(a, lds, wpg, s);
-    case 7: return launch_one<WT, 7>(a, lds, wpg, s);
-    case 8: return launch_one<WT, 8>(a, lds, wpg, s);
+    case 1: return launch_one<WT, 1, XF>(a, lds, wpg, s);
+    case 2: return launch_one<WT, 2, XF>(a, lds, wpg, s);
+    case 3: return launch_one<WT, 3, XF>(a, lds, wpg, s);
+    case 4: return launch_one<WT, 4, XF>(a, lds, wpg, s);
+    case 5: return launch_one<WT, 5, XF>(a, lds, wpg, s);
+    case 6: return launch_one<WT, 6, XF>(a, lds, wpg, s);
+    case 7: return launch_one<WT, 7, XF>(a, lds, wpg, s);
+    case 8: return launch_one<WT, 8, XF>(a, lds, wpg, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int WT>
 hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const int64_t* Ms, const void* xq,
-                      int64_t N, int64_t K, hipStream_t s) {
+                      bool xf32, int64_t N, int64_t K, hipStream_t s) {
     using F = U<WT>;
     const DevInfo& di = dev_info();
     GemvArgs a;
@@ -654,7 +738,7 @@ hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const i
     }
     for (int i = nseg; i < kMaxSeg; ++i) a.seg[i] = a.seg[0];
     a.nwork = work;
-    const int64_t xrowB = (int64_t)a.G * (WT == QMM_Q4_0 || WT == QMM_Q8_0 ? 8 * kQ8_0Bytes : kQ8_KBytes);
+    const int64_t xrowB = xf32 ? K * 4 : (int64_t)a.G * (WT == QMM_Q4_0 || WT == QMM_Q8_0 ? 8 * kQ8_0Bytes : kQ8_KBytes);
     // waves per workgroup: spread small problems over all CUs
     const int64_t per_cu = (work + di.cus - 1) / di.cus;
     const int wpg = per_cu >= 8 ? 8 : per_cu >= 4 ? 4 : per_cu >= 2 ? 2 : 1;
@@ -666,7 +750,7 @@ hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const i
         a.xq = static_cast<const uint8_t*>(xq) + n0 * xrowB;
         for (int i = 0; i < nseg; ++i) a.seg[i].y = ys[i] + n0 * Ms[i];
         for (int i = nseg; i < kMaxSeg; ++i) a.seg[i].y = a.seg[0].y;
-        hipError_t err = dispatch_nc<WT>(nc, a, lds, wpg, s);
+        hipError_t err = xf32 ? dispatch_nc<WT, true>(nc, a, lds, wpg, s) : dispatch_nc<WT, false>(nc, a, lds, wpg, s);
         if (err != hipSuccess) return err;
         n0 += nc;
     }
@@ -692,19 +776,34 @@ bool needs_rowwave(int wtype, int64_t K) {
 
 }  // namespace
 
+bool gemv_fused_supported(int wtype, int64_t K) { return !needs_rowwave(wtype, K); }
+
+hipError_t launch_gemv_multi(int wtype, int count, const void* const* W, float* const* y, const int64_t* M,
+                             const void* x, bool x_f32, int64_t N, int64_t K, hipStream_t s) {
+    if (count < 1 || count > kMaxSeg) return hipErrorInvalidValue;
+    if (needs_rowwave(wtype, K)) {
+        if (x_f32) return hipErrorInvalidValue;
+        for (int i = 0; i < count; ++i) {
+            const hipError_t e = rowwave(wtype, W[i], x, y[i], M[i], N, K, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    switch (wtype) {
+    case QMM_Q4_0: return gemv_typed<QMM_Q4_0>(count, W, y, M, x, x_f32, N, K, s);
+    case QMM_Q8_0: return gemv_typed<QMM_Q8_0>(count, W, y, M, x, x_f32, N, K, s);
+    case QMM_Q4_K: return gemv_typed<QMM_Q4_K>(count, W, y, M, x, x_f32, N, K, s);
+    case QMM_Q6_K: return gemv_typed<QMM_Q6_K>(count, W, y, M, x, x_f32, N, K, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_gemv(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
-    if (needs_rowwave(wtype, K)) return rowwave(wtype, W, xq, y, M, N, K, s);
     const void* Ws[1] = {W};
     float* ys[1] = {y};
     const int64_t Ms[1] = {M};
-    switch (wtype) {
-    case QMM_Q4_0: return gemv_typed<QMM_Q4_0>(1, Ws, ys, Ms, xq, N, K, s);
-    case QMM_Q8_0: return gemv_typed<QMM_Q8_0>(1, Ws, ys, Ms, xq, N, K, s);
-    case QMM_Q4_K: return gemv_typed<QMM_Q4_K>(1, Ws, ys, Ms, xq, N, K, s);
-    case QMM_Q6_K: return gemv_typed<QMM_Q6_K>(1, Ws, ys, Ms, xq, N, K, s);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_gemv_multi(wtype, 1, Ws, ys, Ms, xq, false, N, K, s);
 }
 
 }  // namespace qmm

@@ -99,6 +99,28 @@ int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y, int64_t M, i
     return qmm_mul_mat_algo(wtype, W, xq, y, M, N, K, 0, stream);
 }
 
+int qmm_mul_mat_multi(int wtype, int count, const void* const* W, float* const* y, const int64_t* M,
+                      const void* x, int x_is_f32, int64_t N, int64_t K, void* stream) {
+    if (!is_type(wtype)) return QMM_ERR_TYPE;
+    if (!is_weight(wtype)) return QMM_ERR_UNSUPPORTED;
+    if (count < 1 || count > kMaxMulti) return QMM_ERR_SHAPE;
+    if (!W || !y || !M) return QMM_ERR_NULL;
+    int rc;
+    for (int i = 0; i < count; ++i) {
+        if ((rc = check_ptr(W[i])) || (rc = check_ptr(y[i]))) return rc;
+        if ((rc = check_dims(wtype, M[i], K))) return rc;
+        if (M[i] > INT_MAX) return QMM_ERR_SHAPE;
+    }
+    if ((rc = check_ptr(x))) return rc;
+    const int xt = qmm_vec_dot_type(wtype);
+    if ((rc = check_dims(xt, N, K))) return rc;
+    if (N > INT_MAX) return QMM_ERR_SHAPE;
+    if (K > kMaxK) return QMM_ERR_UNSUPPORTED;
+    if (x_is_f32 && (N > 8 || !gemv_fused_supported(wtype, K))) return QMM_ERR_UNSUPPORTED;
+    return hip_status(launch_gemv_multi(wtype, count, W, y, M, x, x_is_f32 != 0, N, K,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 const char* qmm_strerror(int code) {
     switch (code) {
     case QMM_OK: return "ok";

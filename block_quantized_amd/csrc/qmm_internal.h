@@ -30,6 +30,22 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
 __device__ __forceinline__ uint32_t f2h(float f) {
     return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)f);
 }
+// Round-to-nearest activation code: roundf(t) (half away from zero); NaN
+// (0 * Inf when 1/d overflowed) -> 0; clamp to [-127, 127].  Used by the
+// stand-alone quantizers and by the product's fused quantization alike.
+__device__ __forceinline__ int rtn_code(float t) {
+    float r = roundf(t);
+    if (r != r) return 0;
+    if (r > 127.0f) return 127;
+    if (r < -127.0f) return -127;
+    return (int)r;
+}
+// The block scale and its reciprocal: d = amax / 127 (correctly rounded),
+// id = 1/d, or 0 when d == 0.
+__device__ __forceinline__ void rtn_scale(float amax, float& d, float& id) {
+    d = amax / 127.0f;
+    id = (d != 0.0f) ? 1.0f / d : 0.0f;
+}
 #endif
 
 // ---- launchers (return hipError_t of the launch) ----
@@ -37,6 +53,13 @@ hipError_t launch_quantize(int dst, const float* x, void* out, int64_t rows, int
 hipError_t launch_dequantize(int t, const void* blocks, float* out, int64_t rows, int64_t K, hipStream_t s);
 hipError_t launch_gemv(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s);
+// Several matrices sharing K and x in one launch (count <= kMaxMulti).  x is
+// either quantized activation blocks (x_f32 == false) or fp32 rows that the
+// kernel quantizes itself, bit-identically to launch_quantize (N <= 8 then).
+constexpr int kMaxMulti = 4;
+hipError_t launch_gemv_multi(int wtype, int count, const void* const* W, float* const* y, const int64_t* M,
+                             const void* x, bool x_f32, int64_t N, int64_t K, hipStream_t s);
+bool gemv_fused_supported(int wtype, int64_t K);
 hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s);
 

@@ -146,6 +146,23 @@ int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y,
 int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y,
                      int64_t M, int64_t N, int64_t K, int algo, void* stream);
 
+/* Several weight matrices that share K and the activation rows, in one
+ * launch: e.g. the q, k and v projections of a layer, or its gate and up
+ * projections, which all read the same normalized activations.  Each
+ * matrix i computes y[i] = W[i] x^T exactly as qmm_mul_mat would (the same
+ * values, bit for bit), with M[i] rows.
+ *   count      : 1..4 matrices (QMM_ERR_SHAPE otherwise)
+ *   W, y, M    : host arrays of count device pointers / row counts
+ *   x          : device; with x_is_f32 == 0, N rows of quantized activations
+ *                (as for qmm_mul_mat); with x_is_f32 != 0, N rows of K fp32
+ *                values, which the launch quantizes itself to the
+ *                vec_dot_type with exactly the rule and results of
+ *                qmm_quantize_act (the quantized rows are not written out)
+ * The fp32 form needs N <= 8 and K a multiple of 256 (2048 for Q6_K);
+ * otherwise it returns QMM_ERR_UNSUPPORTED.  Other errors as qmm_mul_mat. */
+int qmm_mul_mat_multi(int wtype, int count, const void* const* W, float* const* y, const int64_t* M,
+                      const void* x, int x_is_f32, int64_t N, int64_t K, void* stream);
+
 /* Static text for a status code. */
 const char* qmm_strerror(int code);
 

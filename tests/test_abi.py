@@ -101,3 +101,19 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         Q.lib()
+
+
+def test_multi_errors_cpu(L):
+    mm = Q.qmm_mul_mat_multi
+    assert mm(99, 1, [A], [A], [4], A, 0, 1, 256, S) == Q.QMM_ERR_TYPE
+    assert mm(Q.QMM_Q8_K, 1, [A], [A], [4], A, 0, 1, 256, S) == Q.QMM_ERR_UNSUPPORTED
+    assert mm(Q.QMM_Q4_K, 0, [A], [A], [4], A, 0, 1, 256, S) == Q.QMM_ERR_SHAPE
+    assert mm(Q.QMM_Q4_K, 5, [A] * 5, [A] * 5, [4] * 5, A, 0, 1, 256, S) == Q.QMM_ERR_SHAPE
+    assert mm(Q.QMM_Q4_K, 1, None, [A], [4], A, 0, 1, 256, S) == Q.QMM_ERR_NULL
+    assert mm(Q.QMM_Q4_K, 2, [A, 0], [A, A], [4, 4], A, 0, 1, 256, S) == Q.QMM_ERR_NULL
+    assert mm(Q.QMM_Q4_K, 2, [A, A + 2], [A, A], [4, 4], A, 0, 1, 256, S) == Q.QMM_ERR_ALIGN
+    assert mm(Q.QMM_Q4_K, 2, [A, A], [A, A], [4, 0], A, 0, 1, 256, S) == Q.QMM_ERR_SHAPE
+    assert mm(Q.QMM_Q4_K, 1, [A], [A], [4], A, 0, 1, 384, S) == Q.QMM_ERR_SHAPE
+    assert mm(Q.QMM_Q4_K, 1, [A], [A], [4], 0, 0, 1, 256, S) == Q.QMM_ERR_NULL
+    assert mm(Q.QMM_Q4_K, 1, [A], [A], [4], A, 1, 9, 256, S) == Q.QMM_ERR_UNSUPPORTED
+    assert mm(Q.QMM_Q4_0, 1, [A], [A], [4], A, 1, 1, 96, S) == Q.QMM_ERR_UNSUPPORTED
