@@ -1,0 +1,245 @@
+// gemm.hip — prefill-path product y = W x^T for many activation rows, on raw
+// GGUF Q4_K blocks, with int8 matrix cores (gfx950 MFMA).
+//
+// Method (page "The GGML ecosystem, and where synapse fits", §5, "Products:
+// weights against quantized activations"): weights stay in their blocks, the
+// activations are Q8_K (int8 codes, fp32 scale per 256, 16-wide integer
+// sums), and each super-block contributes
+//     dx * ( d * sum_j sc_j * P_j  -  dmin * sum_j m_j * S_j )
+// with P_j = sum over sub-block j of q_w * q_x (exact integers) and S_j the
+// activation codes' sum over sub-block j.  Prefill is compute-bound (page
+// "llama.cpp and GGUF": prefill costs about 2 P n FLOPs and is compute-bound),
+// so the contraction runs on v_mfma_i32_32x32x32_i8:
+//
+//  * Exact int8 operands.  sc_j * q (6-bit scale times 4-bit quant, up to 945)
+//    does not fit int8, so the weights enter as two int8 planes,
+//    (sc_j >> 3) * q and (sc_j & 7) * q (each <= 105), and
+//    sum_j sc_j P_j = 8 * P_hi + P_lo, both exact int32 sums over the super-block.
+//  * The min term sum_i m_(i/2) * bsums_i (16 terms) runs on
+//    v_mfma_f32_32x32x16_f16: mins (<= 63) and 16-wide sums (|s| <= 2032) are
+//    exact in fp16 and the fp32 accumulation of 16 products is exact.
+//  * Float scales are applied once per 256-value super-block (epilogue).
+//  * Orientation: the MFMA computes C^T tiles (rows = activation rows n,
+//    columns = weight rows m), so a lane's weight-row scales d, dmin are
+//    per-lane values and its 16 outputs share them.
+//  * A workgroup is 4 wavefronts; each owns 32 weight rows and NT x 32
+//    activation rows.  The activation tile of each super-block is staged once
+//    per workgroup in LDS (double-buffered, one barrier per super-block);
+//    weights are loaded by each lane straight into registers one super-block
+//    ahead (lane l: row l%32, 16 of the 32 bytes of each nibble pair of a
+//    sub-block pair, per the MFMA operand layout: lane l feeds row/column
+//    l%32 and K half l/32; result register r of lane l is row
+//    8(r/4) + 4(l/32) + r%4, column l%32 — checked on the hardware).
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kCodeStride = 272;  // LDS bytes per activation row's 256 codes (+16: bank spread)
+constexpr int kSumStride = 32;    // LDS bytes per activation row's 16 sums as fp16
+
+// bytes b of v (4 quants <= 15) times s (<= 7): each product <= 105 stays in its byte
+__device__ __forceinline__ uint32_t mul_bytes(uint32_t v, uint32_t s) {
+    u16x2 a = __builtin_bit_cast(u16x2, v);
+    u16x2 r = a * (u16x2){(unsigned short)s, (unsigned short)s};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void gemm_q4k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
+                                                       float* __restrict__ Y, int M, int N, int SB) {
+    constexpr int BN = NT * 32;  // activation rows per workgroup
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][kCodeStride];
+    __shared__ __attribute__((aligned(16))) uint8_t s_sums[2][BN][kSumStride];
+    __shared__ __attribute__((aligned(16))) float s_dx[2][BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 31, h = lane >> 5;
+    const int m0 = blockIdx.x * 128 + wave * 32;
+    const int n0 = blockIdx.y * BN;
+    const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
+    const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
+
+    // ---- activation staging: each thread owns (row, half) items
+    constexpr int ITEMS = BN * 2;  // BN rows x 2 halves of 128 codes
+    constexpr int IPT = (ITEMS + 255) / 256;
+    uint32_t xr[IPT][37];
+    auto x_load = [&](int sb) {
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int it = tid + 256 * k;
+            if (it < ITEMS) {
+                const int rn = it >> 1, hf = it & 1;
+                const int n = min(n0 + rn, N - 1);
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(X + ((int64_t)n * SB + sb) * kQ8_KBytes);
+#pragma unroll
+                for (int d = 0; d < 32; ++d) xr[k][d] = p[1 + 32 * hf + d];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) xr[k][32 + d] = p[65 + 4 * hf + d];
+                xr[k][36] = p[0];
+            }
+        }
+    };
+    auto x_store = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int it = tid + 256 * k;
+            if (it < ITEMS) {
+                const int rn = it >> 1, hf = it & 1;
+                uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][128 * hf]);
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+                    dst[d] = make_uint4(xr[k][4 * d], xr[k][4 * d + 1], xr[k][4 * d + 2], xr[k][4 * d + 3]);
+                uint32_t hs[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {  // int16 sums -> fp16 (exact: |s| <= 2032)
+                    const _Float16 lo = (_Float16)(float)(int16_t)(xr[k][32 + d] & 0xFFFF);
+                    const _Float16 hi = (_Float16)(float)(int16_t)(xr[k][32 + d] >> 16);
+                    hs[d] = (uint32_t)__builtin_bit_cast(unsigned short, lo) |
+                            ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
+                }
+                reinterpret_cast<uint4*>(&s_sums[buf][rn][16 * hf])[0] = make_uint4(hs[0], hs[1], hs[2], hs[3]);
+                if (hf == 0) s_dx[buf][rn] = __uint_as_float(xr[k][36]);
+            }
+        }
+    };
+    // ---- weights: header + this lane's halves of the four nibble-pair chunks
+    uint4 wh, wq[4];
+    auto w_load = [&](int sb, uint4& hdr, uint4 (&q)[4]) {
+        const uint8_t* b = wrow + (int64_t)sb * kQ4_KBytes;
+        hdr = reinterpret_cast<const uint4*>(b)[0];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) q[g] = reinterpret_cast<const uint4*>(b + 16 + 32 * g + 16 * h)[0];
+    };
+
+    float yacc[NT][16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
+
+    x_load(0);
+    w_load(0, wh, wq);
+    x_store(0);
+    __syncthreads();
+
+    for (int sb = 0; sb < SB; ++sb) {
+        const int buf = sb & 1;
+        const uint4 hdr = wh;
+        uint4 q[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) q[g] = wq[g];
+        if (sb + 1 < SB) {
+            x_load(sb + 1);
+            w_load(sb + 1, wh, wq);
+        }
+        const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
+        const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
+        const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
+        const uint32_t m47 = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
+
+        // min term: lane K half h covers 16-wide sums 8h..8h+7, i.e. mins 4h..4h+3 twice each
+        const uint32_t mw = h ? m47 : m03;
+        v8h mins;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mins[e] = (_Float16)(float)((mw >> (8 * (e >> 1))) & 0xFF);
+        v16f amin[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const v8h bs = *reinterpret_cast<const v8h*>(&s_sums[buf][32 * t + c][16 * h]);
+            amin[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bs, mins, (v16f){}, 0, 0, 0);
+        }
+
+        v16i ahi[NT], alo[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            ahi[t] = (v16i){};
+            alo[t] = (v16i){};
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint4 qq = q[j >> 1];
+            const int shift = (j & 1) * 4;
+            const uint32_t scw = (j < 4) ? sc03 : sc47;
+            const uint32_t sc = (scw >> (8 * (j & 3))) & 0xFF;
+            const uint32_t sh = sc >> 3, sl = sc & 7;
+            const uint32_t q0 = (qq.x >> shift) & 0x0F0F0F0Fu, q1 = (qq.y >> shift) & 0x0F0F0F0Fu;
+            const uint32_t q2 = (qq.z >> shift) & 0x0F0F0F0Fu, q3 = (qq.w >> shift) & 0x0F0F0F0Fu;
+            const v4i bh = {(int)mul_bytes(q0, sh), (int)mul_bytes(q1, sh), (int)mul_bytes(q2, sh),
+                            (int)mul_bytes(q3, sh)};
+            const v4i bl = {(int)mul_bytes(q0, sl), (int)mul_bytes(q1, sl), (int)mul_bytes(q2, sl),
+                            (int)mul_bytes(q3, sl)};
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const v4i a = *reinterpret_cast<const v4i*>(&s_codes[buf][32 * t + c][32 * j + 16 * h]);
+                ahi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bh, ahi[t], 0, 0, 0);
+                alo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bl, alo[t], 0, 0, 0);
+            }
+        }
+        // epilogue: y[n][m] += dx_n * (d * (8 P_hi + P_lo) - dmin * Smin)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const float4 dx = *reinterpret_cast<const float4*>(&s_dx[buf][32 * t + 8 * qd + 4 * h]);
+                const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * qd + e;
+                    const int u = ahi[t][r] * 8 + alo[t][r];
+                    const float v = (float)u * d - dmin * amin[t][r];
+                    yacc[t][r] += v * dxa[e];
+                }
+            }
+        }
+        if (sb + 1 < SB) x_store(buf ^ 1);
+        __syncthreads();
+    }
+
+    const int m = m0 + c;
+    if (m < M) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = n0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (n < N) Y[(int64_t)n * M + m] = yacc[t][r];
+            }
+    }
+}
+
+}  // namespace
+
+bool gemm_supported(int wtype) { return wtype == QMM_Q4_K; }
+
+hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t s) {
+    if (wtype != QMM_Q4_K) return hipErrorNotSupported;
+    const int SB = (int)(K / 256);
+    const uint8_t* w = static_cast<const uint8_t*>(W);
+    const uint8_t* x = static_cast<const uint8_t*>(xq);
+    // fewer activation rows per workgroup when the weight rows alone would
+    // not give every compute unit a workgroup
+    const int64_t mblocks = (M + 127) / 128;
+    if (mblocks * ((N + 127) / 128) >= 256 || N <= 64) {
+        if (N <= 64) {
+            const dim3 g((unsigned)mblocks, (unsigned)((N + 63) / 64));
+            hipLaunchKernelGGL(gemm_q4k_kernel<2>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, SB);
+        } else {
+            const dim3 g((unsigned)mblocks, (unsigned)((N + 127) / 128));
+            hipLaunchKernelGGL(gemm_q4k_kernel<4>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, SB);
+        }
+    } else {
+        const dim3 g((unsigned)mblocks, (unsigned)((N + 63) / 64));
+        hipLaunchKernelGGL(gemm_q4k_kernel<2>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, SB);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qmm

@@ -90,8 +90,10 @@ int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y, int64_t
     if (M > INT_MAX || N > INT_MAX) return QMM_ERR_SHAPE;
     if (K > kMaxK) return QMM_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (algo == 2) return QMM_ERR_UNSUPPORTED;  // the MFMA GEMM family is not built yet
-    return hip_status(launch_gemv(wtype, W, xq, y, M, N, K, s));
+    const bool has_gemm = gemm_supported(wtype);
+    if (algo == 2 && !has_gemm) return QMM_ERR_UNSUPPORTED;
+    const bool gemm = algo == 2 || (algo == 0 && N > 8 && has_gemm);
+    return hip_status(gemm ? launch_gemm(wtype, W, xq, y, M, N, K, s) : launch_gemv(wtype, W, xq, y, M, N, K, s));
 }
 
 int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,

@@ -60,7 +60,9 @@ constexpr int kMaxMulti = 4;
 hipError_t launch_gemv_multi(int wtype, int count, const void* const* W, float* const* y, const int64_t* M,
                              const void* x, bool x_f32, int64_t N, int64_t K, hipStream_t s);
 bool gemv_fused_supported(int wtype, int64_t K);
+// int8-MFMA product for many activation rows (weight types gemm_supported()).
 hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s);
+bool gemm_supported(int wtype);
 
 }  // namespace qmm

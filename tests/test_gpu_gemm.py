@@ -1,0 +1,83 @@
+"""GPU parity of the int8-MFMA GEMM (Q4_K weights x Q8_K activations).
+
+The product of page 'The GGML ecosystem, and where synapse fits', section 5
+('Products: weights against quantized activations'), on matrix cores: every
+output must satisfy |y - y_ref| <= 1e-5 * T against the CPU oracle, for
+ragged M and N (partial tiles in both directions), both workgroup tile
+widths, and any N through algo=2; results are deterministic and nothing is
+written past y."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_amd as Q
+import oracle as O
+import synth
+from gpu_util import assert_within_tolerance, to_cpu, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def run(W, xq, M, N, K, algo=2):
+    return to_cpu(Q.mul_mat(Q.QMM_Q4_K, to_gpu(W), to_gpu(xq), M, N, K, algo=algo))
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 32, 256), (1, 9, 256), (31, 33, 512), (130, 100, 768), (300, 129, 1024),
+                                   (128, 512, 4096), (4113, 64, 2048), (77, 1, 256), (64, 8, 512), (2000, 200, 256)])
+def test_gemm_q4k_shapes(M, N, K):
+    g = np.random.default_rng(M * 7 + N * 13 + K)
+    W = synth.q4_k_random(g, M, K)
+    x = g.standard_normal((N, K), dtype=np.float32)
+    xq = O.quantize(O.Q8_K, x)
+    print("gemm", M, N, K, flush=True)
+    y = run(W, xq, M, N, K)
+    y_ref, T = O.mul_mat(O.Q4_K, W, xq, M, N, K)
+    assert_within_tolerance(y, y_ref, T, what=f"GEMM {M}x{K} N={N}")
+
+
+def test_gemm_matches_gemv_within_tolerance():
+    g = np.random.default_rng(5)
+    M, N, K = 256, 24, 4096
+    W = synth.q4_k_random(g, M, K)
+    xq = O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32))
+    y_gemm = run(W, xq, M, N, K, algo=2)
+    y_gemv = run(W, xq, M, N, K, algo=1)
+    y_ref, T = O.mul_mat(O.Q4_K, W, xq, M, N, K)
+    assert_within_tolerance(y_gemm, y_ref, T, what="gemm")
+    assert_within_tolerance(y_gemv, y_ref, T, what="gemv")
+    assert np.all(np.abs(y_gemm.astype(np.float64) - y_gemv) <= 2e-5 * T)
+
+
+def test_gemm_extreme_scales_and_zero_rows():
+    # scales and mins at their 6-bit maxima, all nibbles 15: the largest
+    # integer sums the kernel can see; plus an all-zero activation row
+    g = np.random.default_rng(9)
+    M, N, K = 64, 40, 1024
+    W = synth.q4_k_random(g, M, K).reshape(M, K // 256, 144)
+    W[:8, :, 4:16] = 0xFF
+    W[:8, :, 16:] = 0xFF
+    W = W.reshape(M, -1)
+    x = g.standard_normal((N, K), dtype=np.float32)
+    x[3] = 0
+    x[5] = np.sign(x[5]) * 50.0
+    xq = O.quantize(O.Q8_K, x)
+    y = run(W, xq, M, N, K)
+    y_ref, T = O.mul_mat(O.Q4_K, W, xq, M, N, K)
+    assert_within_tolerance(y, y_ref, T, what="extremes")
+    assert np.all(y[3] == 0)
+
+
+def test_gemm_deterministic_and_in_bounds():
+    g = np.random.default_rng(11)
+    M, N, K = 1000, 150, 2048
+    W = to_gpu(synth.q4_k_random(g, M, K))
+    xq = to_gpu(O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32)))
+    outs = []
+    for _ in range(3):
+        buf = torch.full((N * M + 512,), float("nan"), dtype=torch.float32, device=W.device)
+        assert Q.qmm_mul_mat_algo(Q.QMM_Q4_K, W, xq, buf, M, N, K, 2) == Q.QMM_OK
+        b = to_cpu(buf)
+        assert np.all(np.isnan(b[N * M:])), "wrote past the end of y"
+        assert not np.any(np.isnan(b[:N * M]))
+        outs.append(b[:N * M].view(np.uint32).copy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
