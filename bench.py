@@ -22,6 +22,9 @@ prefill), the other GEMV workloads, the dominant kernel's roofline from HIP
 events, and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+       python bench.py --traffic FETCH_CSV WRITE_CSV   (no GPU: summarises two
+           `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of this script
+           into the markdown table kept in profiles/)
 """
 from __future__ import annotations
 
@@ -41,6 +44,10 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
 METRIC = "GEMV effective GB/s (% HBM peak) at batch 1; GEMM int8 TOPS at batch 512"
 
 
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -48,6 +55,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--quick", action="store_true", help="headline only (no secondary workloads)")
+    p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="summarise PMC counter runs (no GPU needed) and exit")
     return p.parse_args()
 
 
@@ -219,6 +228,27 @@ def cpu_baseline_decode(cpu_f32, min_seconds=10.0):
                       f"{reps} passes in {el:.1f} s"}
 
 
+def copy_reference(b: Bench, nbytes=256 << 20, reps=10):
+    """A plain device-to-device copy of known size: its rate is the practical
+    ceiling beside the 8 TB/s peak, and under `rocprofv3 --pmc` its FETCH_SIZE
+    and WRITE_SIZE per dispatch calibrate the counters against known bytes."""
+    torch = b.torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=b.dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "gbs_read_plus_write": round(2 * nbytes * reps / sec / 1e9, 1)}
+
+
 # ------------------------------------------------------- secondary loads
 
 def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=8):
@@ -264,29 +294,116 @@ def secondary(b: Bench):
     out = {}
     q80 = lambda g, M, K: O.quantize(O.Q8_0, synth.normal_f32(g, (M, K), 0.02))
     out["q8_0_gemv_2048x2048_b1"] = gemv_workload(b, b.Q.QMM_Q8_0, 2048, 2048, 1, q80)
+    progress("q8_0 gemv done")
     for (M, K) in synth.LLAMA_8B_SHAPES:
         for N in (1, 4, 8):
             out[f"q4_k_gemv_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q4_K, M, K, N, synth.q4_k_random)
+            progress(f"q4_k gemv {M}x{K} b{N} done")
     M, K = synth.LLAMA_8B_HEAD
     for N in (1, 32):
         out[f"q6_k_head_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q6_K, M, K, N, synth.q6_k_random,
                                                      min_bytes=1, reps_floor=20)
+        progress(f"q6_k head b{N} done")
     for M in (4096, 14336):
         r = gemv_workload(b, b.Q.QMM_Q4_K, M, 4096, 512, synth.q4_k_random, min_bytes=1, reps_floor=5)
         r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
         out[f"q4_k_gemm_{M}x4096_b512"] = r
+        progress(f"q4_k gemm {M}x4096 b512 {r['tops']:.1f} TOPS")
     return out
+
+
+# ------------------------------------------------------- HBM traffic (PMC)
+
+HEAD_KERNEL = "gemv_kernel<1, 1, true>"   # Q4_0, one activation column, fused quantize
+HEAD_SOURCES = ("block_quantized_amd/csrc/gemv.hip", "block_quantized_amd/csrc/qmm_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4_0_decode_sweep_1b_traffic.md")
+COPY_BYTES = 256 << 20
+
+
+def head_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in HEAD_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the head kernel, each
+    scaled by what the same counter reads for the 256 MiB device copy that
+    copy_reference() runs (known bytes), averaged per launch."""
+    import csv
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 0.25 * COPY_BYTES / 1024]
+        head = [float(r["Counter_Value"]) for r in rows if HEAD_KERNEL in r["Kernel_Name"]]
+        if not copy or not head:
+            raise SystemExit(f"{path}: no copy-reference or head-kernel dispatches found")
+        # the copy reads and writes COPY_BYTES each
+        factor = COPY_BYTES / (1024 * sum(copy) / len(copy))
+        per[counter] = {"copy_kib": sum(copy) / len(copy), "factor": factor, "dispatches": len(head),
+                        "head_kib_avg": sum(head) / len(head),
+                        "bytes_per_launch": factor * 1024 * sum(head) / len(head)}
+    total = per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"]
+    rec = {"kernel": HEAD_KERNEL, "sources_sha256_16": head_source_hash(), "bytes_per_launch": round(total),
+           "fetch": per["FETCH_SIZE"], "write": per["WRITE_SIZE"]}
+    print("# HBM traffic: fused Q4_0 GEMV (decode sweep, 1B-Llama shapes, batch 1)\n")
+    print("Counter runs (from the repository root on one MI355X, each a run of its own):\n")
+    print("```")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        print(f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c.split('_')[0].lower()} -o run --output-format csv "
+              "-- python -u bench.py --quick --no-cpu --steps 2 --warmup 1")
+    print("python bench.py --traffic gpurun_out/pmc_fetch/run_counter_collection.csv "
+          "gpurun_out/pmc_write/run_counter_collection.csv")
+    print("```\n")
+    print("| counter | 256 MiB copy, counter (KiB) | scale factor | head dispatches | head avg (KiB) | bytes per launch |")
+    print("|---|---|---|---|---|---|")
+    for c, v in per.items():
+        print(f"| {c} | {v['copy_kib']:.1f} | {v['factor']:.4f} | {v['dispatches']} | {v['head_kib_avg']:.1f} | "
+              f"{v['bytes_per_launch']:.0f} |")
+    print(f"\nTraffic per launch (scaled fetch + write): {total:.0f} B.\n")
+    print(f"<!-- traffic: {json.dumps(rec)} -->")
+
+
+def recorded_traffic():
+    """Bytes per launch from the committed counter summary, or None when the
+    head kernel's sources changed since the counters were taken."""
+    import re
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, None
+    m = re.search(r"<!-- traffic: (\{.*\}) -->", open(TRAFFIC_FILE).read())
+    if not m:
+        return None, None
+    rec = json.loads(m.group(1))
+    if rec.get("sources_sha256_16") != head_source_hash():
+        return None, rec
+    return rec["bytes_per_launch"], rec
 
 
 def main():
     a = parse()
+    if a.traffic:
+        traffic_summary(*a.traffic)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the product shards by output "
               "rows with no exchange, so N GPUs would each run this workload on M/N rows.", file=sys.stderr)
         sys.exit(2)
     b = Bench()
+    copy = copy_reference(b)
+    progress(f"copy reference {copy['gbs_read_plus_write']} GB/s")
     head, cpu_f32 = decode_sweep(b, a.steps, a.warmup, keep_cpu_layers=0 if a.no_cpu else 2)
+    progress(f"decode sweep {head['gbs']:.1f} GB/s, {head['ms_per_step']:.4f} ms/step")
     gemv_us = head["seconds"] / (a.steps * head["launches_per_step"]) * 1e6
+    traffic, rec = recorded_traffic()
+    if traffic is not None:
+        traffic_note = (f"HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a 256 MiB copy "
+                        f"({os.path.relpath(TRAFFIC_FILE, ROOT)}); algorithmic bytes per launch "
+                        f"{head['bytes_step'] / head['launches_per_step']:.0f}")
+    else:
+        traffic_note = "no counter run for the current kernel sources" if rec else "no counter run recorded"
     line = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -318,10 +435,12 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(head["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_note": traffic_note,
             "avg_launch_us": round(gemv_us, 3),
             "launches": head["launches_per_step"] * a.steps,
         },
+        "copy_reference": copy,
     }
     if not a.quick:
         sec = secondary(b)
@@ -334,6 +453,7 @@ def main():
             "peak": INT8_PEAK_TOPS,
         }
     if not a.no_cpu:
+        progress("timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline_decode(cpu_f32)
     print(json.dumps(line))
 
