@@ -95,17 +95,28 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
     constexpr int KB = XF ? 1 : 4;  // items per thread per round
     const int nitems = kQ80 ? NC * G * 8 : NC * G * 4;
     const int step = KB * blockDim.x;
-    for (int base = 0, round = 0; base < nitems || round == 0; base += step, ++round) {
+    // A wave issues its loads when any of its lanes has an item (a lane past
+    // the last item re-reads the last item and stores nothing); a wave with no
+    // item skips them as a whole.  No lane-level branch guards a load, so the
+    // waits retire exactly the loads they need - in particular, waiting for x
+    // does not wait for the W prefetch issued after it.
+    const int wave0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x) & ~63;  // first thread of this wave
+    auto round = [&](const int base, auto first) {
+        constexpr bool kFirst = decltype(first)::value;
         if constexpr (XF && kQ80) {
             // fp32 rows quantized here to Q8_0, exactly as the stand-alone
             // quantizer does: item i = values 32i .. 32i+31.
             const int i = base + threadIdx.x;
+            const int ic = i < nitems ? i : nitems - 1;
             float4 v[8];
-            if (i < nitems) {
+            if (base + wave0 < nitems) {
 #pragma unroll
-                for (int h = 0; h < 8; ++h) v[h] = reinterpret_cast<const float4*>(xq)[8 * i + h];
+                for (int h = 0; h < 8; ++h) v[h] = reinterpret_cast<const float4*>(xq)[8 * ic + h];
             }
-            if (round == 0) after_loads();
+            if constexpr (kFirst) {
+                __builtin_amdgcn_sched_barrier(0);  // keep x's loads ahead of W's (loads retire in order)
+                after_loads();
+            }
             if (i < nitems) {
                 float amax = 0.0f;
 #pragma unroll
@@ -134,13 +145,17 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
             // i>>2 (values 64i .. 64i+63); the four quarters of a block are
             // adjacent lanes and share the block maximum through shuffles.
             const int i = base + threadIdx.x;
+            const int ic = i < nitems ? i : nitems - 1;
             float4 v[16];
             float amax = 0.0f;
-            if (i < nitems) {
+            if (base + wave0 < nitems) {
 #pragma unroll
-                for (int h = 0; h < 16; ++h) v[h] = reinterpret_cast<const float4*>(xq)[16 * i + h];
+                for (int h = 0; h < 16; ++h) v[h] = reinterpret_cast<const float4*>(xq)[16 * ic + h];
             }
-            if (round == 0) after_loads();
+            if constexpr (kFirst) {
+                __builtin_amdgcn_sched_barrier(0);  // keep x's loads ahead of W's (loads retire in order)
+                after_loads();
+            }
             if (i < nitems) {
 #pragma unroll
                 for (int h = 0; h < 16; ++h)
@@ -184,13 +199,17 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
                 const int i = base + k * blockDim.x + threadIdx.x;
-                if (i < nitems) {
-                    const uint16_t* p = reinterpret_cast<const uint16_t*>(xq + (int64_t)i * kQ8_0Bytes);
+                const int ic = i < nitems ? i : nitems - 1;
+                const uint16_t* p = reinterpret_cast<const uint16_t*>(xq + (int64_t)ic * kQ8_0Bytes);
+                if (base + k * (int)blockDim.x + wave0 < nitems) {
 #pragma unroll
                     for (int h = 0; h < 17; ++h) v[k][h] = p[h];
                 }
             }
-            if (round == 0) after_loads();
+            if constexpr (kFirst) {
+                __builtin_amdgcn_sched_barrier(0);  // keep x's loads ahead of W's (loads retire in order)
+                after_loads();
+            }
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
                 const int i = base + k * blockDim.x + threadIdx.x;
@@ -215,9 +234,10 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
                 const int i = base + k * blockDim.x + threadIdx.x;
-                if (i < nitems) {
-                    const uint32_t* p = reinterpret_cast<const uint32_t*>(xq + (int64_t)(i >> 2) * kQ8_KBytes);
-                    const int qq = i & 3;
+                const int ic = i < nitems ? i : nitems - 1;
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(xq + (int64_t)(ic >> 2) * kQ8_KBytes);
+                const int qq = ic & 3;
+                if (base + k * (int)blockDim.x + wave0 < nitems) {
 #pragma unroll
                     for (int d = 0; d < 16; ++d) v[k][d] = p[1 + 16 * qq + d];
                     v[k][16] = p[65 + 2 * qq];  // bsums 4qq .. 4qq+3
@@ -225,7 +245,10 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
                     v[k][18] = p[0];            // fp32 d
                 }
             }
-            if (round == 0) after_loads();
+            if constexpr (kFirst) {
+                __builtin_amdgcn_sched_barrier(0);  // keep x's loads ahead of W's (loads retire in order)
+                after_loads();
+            }
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
                 const int i = base + k * blockDim.x + threadIdx.x;
@@ -252,7 +275,9 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
                 }
             }
         }
-    }
+    };
+    round(0, std::true_type{});
+    for (int base = step; base < nitems; base += step) round(base, std::false_type{});
 }
 
 // ------------------------------------------------------- unit compute
@@ -450,13 +475,22 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     const bool lwriter = (lane & (P - 1)) == 0 && lr < RW;
 
     // Where this lane's unit lies.
+    // Loads and stores are never skipped by a branch: a lane without a unit
+    // reads a unit that exists (the first of segment 0) and discards it, and
+    // outputs go through a buffer store whose offset is out of range for
+    // lanes that must not write, which the hardware drops.  So the count of
+    // memory operations in flight is the same on every path, and the
+    // compiler's waits retire only the loads actually needed next.
+    constexpr int kNoStore = 1 << 30;
     struct Loc {
-        const uint8_t* p;  // first byte of the unit (16-byte aligned), or null if none
-        float* y;          // output row base for this lane's row (lane 0 of the row writes)
+        const uint8_t* p;  // first byte of the unit (16-byte aligned); a dummy unit if !valid
+        float* yb;         // output of the chunk's first row (wave-uniform)
         int64_t ldy;       // stride between output columns (the segment's M)
+        int nrec;          // bytes of output rows of this chunk that exist (wave-uniform)
+        int yoff;          // this lane's byte offset from yb, or kNoStore
         int g;             // first 256-value activation group of the unit
         bool last;         // last chunk of its work item
-        bool writer;
+        bool valid;
     };
     auto locate = [&](int64_t wi, int kc) {  // work item wi (uniform), chunk kc of it
         Loc L;
@@ -475,31 +509,30 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         const int gu = kc * 64 + lg;  // kc is 0 when a row fits one chunk
         const int64_t row = row0 + lr;
         const bool valid = gu < GU && lr < RW && row < M;
-        L.p = valid ? W + row * rowB + (int64_t)gu * F::UB : nullptr;
-        L.y = Y + row;
+        L.valid = valid;
+        L.p = valid ? W + row * rowB + (int64_t)gu * F::UB : sW[0];
+        L.yb = Y + row0;
         L.ldy = M;
+        const int64_t left = M - row0;  // >= 1
+        L.nrec = 4 * (int)(left < RW ? left : RW);
+        L.yoff = lwriter ? 4 * lr : kNoStore;
         L.g = gu * (F::WPU / 256);
         L.last = kc == NKC - 1;
-        L.writer = lwriter && row < M;
         return L;
     };
     // Sub-step j of a unit: a window of NV 16-byte pieces.
     auto load = [&](const Loc& L, int j, uint4 (&v)[NV]) {
-        if (L.p) {
-            const uint4* q = reinterpret_cast<const uint4*>(L.p + (SUB > 1 ? ((kQ6_KBytes * j) & ~15) : 0));
+        const uint4* q = reinterpret_cast<const uint4*>(L.p + (SUB > 1 ? ((kQ6_KBytes * j) & ~15) : 0));
 #pragma unroll
-            for (int i = 0; i < NV; ++i) v[i] = q[i];
-        }
+        for (int i = 0; i < NV; ++i) v[i] = q[i];
     };
 
     uint4 buf[2][NV];
     Loc cur, nxt;
     int64_t nwi = gw;  // position of `nxt`: work item and chunk
     int pkc = 0;
-    if (gw < nwork) nxt = locate(gw, 0);
-    stage_x<WT, NC, XF>(xq, G, xl, [&]() {
-        if (gw < nwork) load(nxt, 0, buf[0]);
-    });
+    nxt = locate(gw < nwork ? gw : nwork - 1, 0);
+    stage_x<WT, NC, XF>(xq, G, xl, [&]() { load(nxt, 0, buf[0]); });
     __syncthreads();
     if (gw >= nwork) return;  // no barrier follows
 
@@ -510,11 +543,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
 
     // One sub-step: prefetch the next sub-step into the other buffer, then
     // compute sub-step J of `cur` from buffer B.  J and B are compile-time.
-    auto step = [&](auto tag, bool more) {
+    auto step = [&](auto tag, auto more) {
         constexpr int J = decltype(tag)::j, B = decltype(tag)::b;
         if constexpr (J + 1 < SUB) load(cur, J + 1, buf[B ^ 1]);
-        else if (more) load(nxt, 0, buf[B ^ 1]);
-        if (cur.p) {
+        else if constexpr (decltype(more)::value) load(nxt, 0, buf[B ^ 1]);
+        if (cur.valid) {
             const uint32_t* w = reinterpret_cast<const uint32_t*>(buf[B]);
             const uint8_t* xr0 = xl + (cur.g + J) * XREC;
             if constexpr (WT == QMM_Q4_0) unit_q4_0<NC>(w, xr0, xstride, acc);
@@ -526,14 +559,15 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     // After the last chunk of a work item: butterfly over the P lanes of
     // each row, then one lane stores.
     auto finish = [&]() {
-        if (cur.last) {
+        const int off = cur.last ? cur.yoff : kNoStore;
 #pragma unroll
-            for (int n = 0; n < NC; ++n) {
-                float v = acc[n];
-                for (int o = P >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
-                if (cur.writer) cur.y[n * cur.ldy] = v;
-                acc[n] = 0.f;
-            }
+        for (int n = 0; n < NC; ++n) {
+            float v = acc[n];
+            for (int o = P >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
+            const __amdgpu_buffer_rsrc_t r =
+                __builtin_amdgcn_make_buffer_rsrc(cur.yb + n * cur.ldy, (short)0, cur.nrec, kBufferWord3);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+            acc[n] = cur.last ? 0.f : acc[n];
         }
     };
     auto advance = [&]() {  // make `nxt` current and locate the unit after it
@@ -547,30 +581,42 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         return more;
     };
 
+    // The last unit of a wave is computed by its own copy of the step, which
+    // issues no further load (a uniform branch, taken once per wave).
     if constexpr (SUB == 1) {
         for (;;) {
-            bool more = advance();
-            step(Tag<0, 0>{}, more);
+            if (!advance()) {
+                step(Tag<0, 0>{}, std::false_type{});
+                finish();
+                break;
+            }
+            step(Tag<0, 0>{}, std::true_type{});
             finish();
-            if (!more) break;
-            more = advance();
-            step(Tag<0, 1>{}, more);
+            if (!advance()) {
+                step(Tag<0, 1>{}, std::false_type{});
+                finish();
+                break;
+            }
+            step(Tag<0, 1>{}, std::true_type{});
             finish();
-            if (!more) break;
         }
     } else {
         for (;;) {
             const bool more = advance();
-            step(Tag<0, 0>{}, more);
-            step(Tag<1, 1>{}, more);
-            step(Tag<2, 0>{}, more);
-            step(Tag<3, 1>{}, more);
-            step(Tag<4, 0>{}, more);
-            step(Tag<5, 1>{}, more);
-            step(Tag<6, 0>{}, more);
-            step(Tag<7, 1>{}, more);
+            step(Tag<0, 0>{}, std::true_type{});
+            step(Tag<1, 1>{}, std::true_type{});
+            step(Tag<2, 0>{}, std::true_type{});
+            step(Tag<3, 1>{}, std::true_type{});
+            step(Tag<4, 0>{}, std::true_type{});
+            step(Tag<5, 1>{}, std::true_type{});
+            step(Tag<6, 0>{}, std::true_type{});
+            if (!more) {
+                step(Tag<7, 1>{}, std::false_type{});
+                finish();
+                break;
+            }
+            step(Tag<7, 1>{}, std::true_type{});
             finish();
-            if (!more) break;
         }
     }
 }

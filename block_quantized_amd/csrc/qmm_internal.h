@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/qmm.h"
 
 namespace qmm {
@@ -33,13 +35,15 @@ __device__ __forceinline__ uint32_t f2h(float f) {
 // Round-to-nearest activation code: roundf(t) (half away from zero); NaN
 // (0 * Inf when 1/d overflowed) -> 0; clamp to [-127, 127].  Used by the
 // stand-alone quantizers and by the product's fused quantization alike.
+// Branch-free: v_med3 clamps (+-Inf -> +-127) and a select maps NaN to 0.
 __device__ __forceinline__ int rtn_code(float t) {
-    float r = roundf(t);
-    if (r != r) return 0;
-    if (r > 127.0f) return 127;
-    if (r < -127.0f) return -127;
-    return (int)r;
+    const float r = __builtin_amdgcn_fmed3f(roundf(t), -127.0f, 127.0f);
+    return (t == t) ? (int)r : 0;
 }
+// Word 3 of a raw buffer resource on gfx9-family chips (gfx950 included):
+// 32-bit data format, no swizzle.  With stride 0, an access at or past
+// num_records bytes is out of range: loads return 0 and stores are dropped.
+constexpr int kBufferWord3 = 0x00020000;
 // The block scale and its reciprocal: d = amax / 127 (correctly rounded),
 // id = 1/d, or 0 when d == 0.
 __device__ __forceinline__ void rtn_scale(float amax, float& d, float& id) {
