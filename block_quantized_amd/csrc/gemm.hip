@@ -30,12 +30,24 @@
 //    sub-block pair, per the MFMA operand layout: lane l feeds row/column
 //    l%32 and K half l/32; result register r of lane l is row
 //    8(r/4) + 4(l/32) + r%4, column l%32 — checked on the hardware).
+//
+// Q6_K weights (w = d * sc_j * (q - 32), 16-value sub-blocks with int8
+// scales; the offset 32 is this library's reading of the format table) take
+// v_mfma_i32_32x32x16_i8, one per sub-block: the weights enter as the int8
+// values q - 32 (in [-32, 31]), so no activation sums are needed, and since
+// sc_j * (q - 32) does not fit int8 the per-sub-block scale is applied to the
+// int32 tile by VALU (acc += sc_j * P_j, exact).  At the batch this serves
+// (the 32-row output head) the kernel is bound by streaming W, and those
+// VALU operations hide under the loads.
 #include "qmm_internal.h"
 
 namespace qmm {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+// 8 and 16 bytes at a 2-byte-aligned address (Q6_K super-blocks are 210 bytes)
+typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -214,19 +226,181 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(const uint8_t* __restrict
     }
 }
 
+// ------------------------------------------------------------------ Q6_K
+// Lane l = (c = l%32, h = l/32) feeds weight row m0 + c and, for sub-block j
+// (values 16j .. 16j+15 of the super-block), the 8 values 16j + 8h .. +7.
+// In the block those values' low 4 bits are 8 consecutive nibbles of ql and
+// their high 2 bits a 2-bit field of 8 consecutive qh bytes, so a lane reads
+// 8 ql chunks and 4 qh chunks of 8 bytes per super-block, plus the 16 scales
+// and d.  The activation operand holds the same 8 codes of the same
+// sub-block (any consistent assignment of k to lanes gives the same sum).
+template <int NT>
+__global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
+                                                       float* __restrict__ Y, int M, int N, int SB) {
+    constexpr int BN = NT * 32;
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][kCodeStride];
+    __shared__ __attribute__((aligned(16))) float s_dx[2][BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 31, h = lane >> 5;
+    const int m0 = blockIdx.x * 128 + wave * 32;
+    const int n0 = blockIdx.y * BN;
+    const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
+    const uint8_t* wrow = W + (int64_t)mrow * SB * kQ6_KBytes;
+
+    // ---- activation staging: (row, half) items of 128 codes, plus d
+    constexpr int ITEMS = BN * 2;
+    constexpr int IPT = (ITEMS + 255) / 256;
+    uint32_t xr[IPT][33];
+    auto x_load = [&](int sb) {
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int it = tid + 256 * k;
+            if (it < ITEMS) {
+                const int rn = it >> 1, hf = it & 1;
+                const int n = min(n0 + rn, N - 1);
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(X + ((int64_t)n * SB + sb) * kQ8_KBytes);
+#pragma unroll
+                for (int d = 0; d < 32; ++d) xr[k][d] = p[1 + 32 * hf + d];
+                xr[k][32] = p[0];
+            }
+        }
+    };
+    auto x_store = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int it = tid + 256 * k;
+            if (it < ITEMS) {
+                const int rn = it >> 1, hf = it & 1;
+                uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][128 * hf]);
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+                    dst[d] = make_uint4(xr[k][4 * d], xr[k][4 * d + 1], xr[k][4 * d + 2], xr[k][4 * d + 3]);
+                if (hf == 0) s_dx[buf][rn] = __uint_as_float(xr[k][32]);
+            }
+        }
+    };
+    // ---- weights: ql chunk (h2, c&1, p) at 64 h2 + 32 (c&1) + 16 p + 8h;
+    //      qh chunk (h2, p) at 128 + 32 h2 + 16 p + 8h; scales; d
+    struct WQ {
+        u32x2_a2 ql[8], qh[4];
+        u32x4_a2 sc;
+        uint32_t d;
+    };
+    WQ wn;
+    auto w_load = [&](int sb, WQ& w) {
+        const uint8_t* b = wrow + (int64_t)sb * kQ6_KBytes + 8 * h;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w.ql[i] = *reinterpret_cast<const u32x2_a2*>(b + 16 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.qh[i] = *reinterpret_cast<const u32x2_a2*>(b + 128 + 16 * i);
+        w.sc = *reinterpret_cast<const u32x4_a2*>(b - 8 * h + 192);
+        w.d = *reinterpret_cast<const uint16_t*>(b - 8 * h + 208);
+    };
+
+    float yacc[NT][16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
+
+    x_load(0);
+    w_load(0, wn);
+    x_store(0);
+    __syncthreads();
+
+    for (int sb = 0; sb < SB; ++sb) {
+        const int buf = sb & 1;
+        const WQ w = wn;
+        if (sb + 1 < SB) {
+            x_load(sb + 1);
+            w_load(sb + 1, wn);
+        }
+        int acc[NT][16];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][r] = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int h2 = j >> 3, cc = (j >> 1) & 3, p = j & 1;
+            const u32x2_a2 lq = w.ql[4 * h2 + 2 * (cc & 1) + p];
+            const u32x2_a2 hq = w.qh[2 * h2 + p];
+            const int ls = (cc >> 1) * 4;  // c < 2: low nibbles, else high
+            uint32_t b[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t lo = (lq[e] >> ls) & 0x0F0F0F0Fu;
+                const uint32_t hi = (hq[e] >> (2 * cc)) & 0x03030303u;
+                // byte (hi - 2) * 16 from a 4-entry byte table: E0 F0 00 10
+                b[e] = lo | __builtin_amdgcn_perm(0u, 0x1000F0E0u, hi);
+            }
+            const long bq = (long)(((uint64_t)b[1] << 32) | b[0]);
+            const int sc = (int)(int8_t)(w.sc[j >> 2] >> (8 * (j & 3)));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const long a = *reinterpret_cast<const long*>(&s_codes[buf][32 * t + c][16 * j + 8 * h]);
+                const v16i tile = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, (v16i){}, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] += sc * tile[r];
+            }
+        }
+        // epilogue: y[n][m] += (d * dx_n) * sum_j sc_j * P_j   (the integer sum is exact)
+        const float dw = h2f(w.d);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const float4 dx = *reinterpret_cast<const float4*>(&s_dx[buf][32 * t + 8 * qd + 4 * h]);
+                const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * qd + e;
+                    yacc[t][r] += (dw * dxa[e]) * (float)acc[t][r];
+                }
+            }
+        }
+        if (sb + 1 < SB) x_store(buf ^ 1);
+        __syncthreads();
+    }
+
+    const int m = m0 + c;
+    if (m < M) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = n0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (n < N) Y[(int64_t)n * M + m] = yacc[t][r];
+            }
+    }
+}
+
 }  // namespace
 
-bool gemm_supported(int wtype) { return wtype == QMM_Q4_K; }
+bool gemm_supported(int wtype) { return wtype == QMM_Q4_K || wtype == QMM_Q6_K; }
 
 hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
-    if (wtype != QMM_Q4_K) return hipErrorNotSupported;
+    if (!gemm_supported(wtype)) return hipErrorNotSupported;
     const int SB = (int)(K / 256);
     const uint8_t* w = static_cast<const uint8_t*>(W);
     const uint8_t* x = static_cast<const uint8_t*>(xq);
+    const int64_t mblocks = (M + 127) / 128;
+    if (wtype == QMM_Q6_K) {
+        // bound by streaming W: one 32-row activation tile per workgroup up to
+        // N = 32 (W read once), wider tiles beyond
+        if (N <= 32) {
+            hipLaunchKernelGGL(gemm_q6k_kernel<1>, dim3((unsigned)mblocks, 1), dim3(256), 0, s, w, x, y, (int)M,
+                               (int)N, SB);
+        } else {
+            hipLaunchKernelGGL(gemm_q6k_kernel<2>, dim3((unsigned)mblocks, (unsigned)((N + 63) / 64)), dim3(256), 0,
+                               s, w, x, y, (int)M, (int)N, SB);
+        }
+        return hipGetLastError();
+    }
     // fewer activation rows per workgroup when the weight rows alone would
     // not give every compute unit a workgroup
-    const int64_t mblocks = (M + 127) / 128;
     if (mblocks * ((N + 127) / 128) >= 256 || N <= 64) {
         if (N <= 64) {
             const dim3 g((unsigned)mblocks, (unsigned)((N + 63) / 64));

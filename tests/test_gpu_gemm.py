@@ -81,3 +81,74 @@ def test_gemm_deterministic_and_in_bounds():
         assert not np.any(np.isnan(b[:N * M]))
         outs.append(b[:N * M].view(np.uint32).copy())
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+# ------------------------------------------------------------------ Q6_K
+
+def run_q6k(W, xq, M, N, K, algo=2):
+    return to_cpu(Q.mul_mat(Q.QMM_Q6_K, to_gpu(W), to_gpu(xq), M, N, K, algo=algo))
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 32, 256), (1, 9, 256), (31, 33, 512), (130, 100, 768), (300, 32, 2048),
+                                   (129, 65, 256), (77, 1, 256), (4100, 32, 4096), (64, 8, 1280)])
+def test_gemm_q6k_shapes(M, N, K):
+    g = np.random.default_rng(M * 5 + N * 17 + K)
+    W = synth.q6_k_random(g, M, K)
+    x = g.standard_normal((N, K), dtype=np.float32)
+    xq = O.quantize(O.Q8_K, x)
+    print("gemm q6_k", M, N, K, flush=True)
+    y = run_q6k(W, xq, M, N, K)
+    y_ref, T = O.mul_mat(O.Q6_K, W, xq, M, N, K)
+    assert_within_tolerance(y, y_ref, T, what=f"Q6_K GEMM {M}x{K} N={N}")
+
+
+def test_gemm_q6k_extreme_scales():
+    # int8 scale extremes (-128, 127), all-ones and all-zero 6-bit codes, a
+    # large activation row and a zero row
+    g = np.random.default_rng(21)
+    M, N, K = 96, 40, 1024
+    W = synth.q6_k_random(g, M, K).reshape(M, K // 256, 210)
+    W[:16, :, 192:208] = np.array([0x80, 0x7F] * 8, dtype=np.uint8)
+    W[:8, :, :192] = 0xFF      # q = 63
+    W[8:16, :, :192] = 0x00    # q = 0
+    W = W.reshape(M, -1)
+    x = g.standard_normal((N, K), dtype=np.float32)
+    x[3] = 0
+    x[5] = np.sign(x[5]) * 50.0
+    xq = O.quantize(O.Q8_K, x)
+    y = run_q6k(W, xq, M, N, K)
+    y_ref, T = O.mul_mat(O.Q6_K, W, xq, M, N, K)
+    assert_within_tolerance(y, y_ref, T, what="Q6_K extremes")
+    assert np.all(y[3] == 0)
+
+
+def test_gemm_q6k_head_sampled():
+    # the 128256 x 4096 output head at batch 32, as the automatic choice runs
+    # it, checked on sampled rows against the oracle
+    g = np.random.default_rng(0)
+    M, K = 128256, 4096
+    N = 32
+    W = synth.q6_k_random(g, M, K)
+    xq = O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32))
+    y = to_cpu(Q.mul_mat(Q.QMM_Q6_K, to_gpu(W), to_gpu(xq), M, N, K))
+    rows = np.unique(np.concatenate([np.arange(8), M - 1 - np.arange(8), g.integers(0, M, 48)]))
+    y_ref, T = O.mul_mat(O.Q6_K, np.ascontiguousarray(W[rows]), xq, len(rows), N, K)
+    assert_within_tolerance(y[:, rows], y_ref, T, what="Q6_K head N=32 (sampled rows)")
+
+
+def test_gemm_q6k_deterministic_in_bounds_and_matches_gemv():
+    g = np.random.default_rng(23)
+    M, N, K = 700, 50, 2048
+    W = to_gpu(synth.q6_k_random(g, M, K))
+    xq = to_gpu(O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32)))
+    outs = []
+    for _ in range(2):
+        buf = torch.full((N * M + 512,), float("nan"), dtype=torch.float32, device=W.device)
+        assert Q.qmm_mul_mat_algo(Q.QMM_Q6_K, W, xq, buf, M, N, K, 2) == Q.QMM_OK
+        b = to_cpu(buf)
+        assert np.all(np.isnan(b[N * M:])), "wrote past the end of y"
+        outs.append(b[:N * M])
+    assert np.array_equal(outs[0], outs[1])
+    y_gemv = to_cpu(Q.mul_mat(Q.QMM_Q6_K, W, xq, M, N, K, algo=1)).reshape(-1)
+    y_ref, T = O.mul_mat(O.Q6_K, to_cpu(W), to_cpu(xq), M, N, K)
+    assert np.all(np.abs(outs[0].astype(np.float64) - y_gemv) <= 2e-5 * T.reshape(-1))
