@@ -24,7 +24,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
 UNITS = {
     "codec.hip": ["-ffp-contract=off"],
     "gemv.hip": [],
-    "gemm.hip": [],
+    # MFMA results in VGPRs (not AGPRs): the epilogue reads them without
+    # v_accvgpr_read, and register use drops enough for 2 waves per SIMD
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "qmm.cpp": [],
 }
 
@@ -49,7 +51,9 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(units))) as ex:
         objs = list(ex.map(lambda kv: _compile(*kv), units.items()))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # --no-undefined: a kernel whose host stub failed to emit must fail the
+    # build here, not the first dlopen
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     if verbose:

@@ -53,6 +53,16 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// Makes `v` depend on `acc`, so that the matrix instruction consuming `v` is
+// issued after the VALU work that produced `acc` (device code only; an empty
+// asm statement emits no instruction).
+template <class T>
+__device__ __forceinline__ void order_after(long& v, const T& acc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(v) : "v"(acc));
+#endif
+}
+
 constexpr int kCodeStride = 272;  // LDS bytes per activation row's 256 codes (+16: bank spread)
 constexpr int kSumStride = 32;    // LDS bytes per activation row's 16 sums as fp16
 
@@ -316,13 +326,11 @@ __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict
             x_load(sb + 1);
             w_load(sb + 1, wn);
         }
-        int acc[NT][16];
+        v16i acc[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[t][r] = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int t = 0; t < NT; ++t) acc[t] = (v16i){};
+        // sub-block j's weight operand: the int8 values q - 32 of its 8 elements
+        auto operand = [&](const int j) {
             const int h2 = j >> 3, cc = (j >> 1) & 3, p = j & 1;
             const u32x2_a2 lq = w.ql[4 * h2 + 2 * (cc & 1) + p];
             const u32x2_a2 hq = w.qh[2 * h2 + p];
@@ -335,15 +343,38 @@ __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict
                 // byte (hi - 2) * 16 from a 4-entry byte table: E0 F0 00 10
                 b[e] = lo | __builtin_amdgcn_perm(0u, 0x1000F0E0u, hi);
             }
-            const long bq = (long)(((uint64_t)b[1] << 32) | b[0]);
+            return (long)(((uint64_t)b[1] << 32) | b[0]);
+        };
+        auto product = [&](const int j, const int t, const long bq) {
+            const long a = *reinterpret_cast<const long*>(&s_codes[buf][32 * t + c][16 * j + 8 * h]);
+            return __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, (v16i){}, 0, 0, 0);
+        };
+        // Software pipeline: the tile of sub-block j+1 is issued before the
+        // scale of sub-block j is applied, so the matrix core and the VALU
+        // overlap and at most two tiles per activation tile are live.  (The
+        // empty asm makes the operand of tile j+2 wait for the scaling of
+        // tile j; without it the compiler issues all 16 tiles first and
+        // holds them in 256 registers.)
+        v16i tl[2][NT];
+        {
+            const long bq = operand(0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) tl[0][t] = product(0, t, bq);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j + 1 < 16) {
+                long bq = operand(j + 1);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) order_after(bq, acc[t]);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) tl[(j + 1) & 1][t] = product(j + 1, t, bq);
+            }
             const int sc = (int)(int8_t)(w.sc[j >> 2] >> (8 * (j & 3)));
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const long a = *reinterpret_cast<const long*>(&s_codes[buf][32 * t + c][16 * j + 8 * h]);
-                const v16i tile = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, (v16i){}, 0, 0, 0);
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[t][r] += sc * tile[r];
-            }
+                for (int r = 0; r < 16; ++r) acc[t][r] = __mul24(sc, tl[j & 1][t][r]) + acc[t][r];  // |tile| < 2^17
         }
         // epilogue: y[n][m] += (d * dx_n) * sum_j sc_j * P_j   (the integer sum is exact)
         const float dw = h2f(w.d);
