@@ -48,6 +48,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // 8 and 16 bytes at a 2-byte-aligned address (Q6_K super-blocks are 210 bytes)
 typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+// 8 and 16 bytes at a 4-byte-aligned address (Q8_K blocks are 292 bytes)
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -74,7 +77,7 @@ __device__ __forceinline__ uint32_t mul_bytes(uint32_t v, uint32_t s) {
 }
 
 template <int NT>
-__global__ __launch_bounds__(256) void gemm_q4k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
+__global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
                                                        float* __restrict__ Y, int M, int N, int SB) {
     constexpr int BN = NT * 32;  // activation rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][kCodeStride];
@@ -88,23 +91,25 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(const uint8_t* __restrict
     const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
     const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
 
-    // ---- activation staging: each thread owns (row, half) items
-    constexpr int ITEMS = BN * 2;  // BN rows x 2 halves of 128 codes
+    // ---- activation staging: every thread owns (row, quarter) items: 64
+    //      codes, their 4 sums, and (quarter 0) the scale; 16-byte loads
+    constexpr int ITEMS = BN * 4;
     constexpr int IPT = (ITEMS + 255) / 256;
-    uint32_t xr[IPT][37];
+    u32x4_a4 xc[IPT][4];
+    u32x2_a4 xs[IPT];
+    uint32_t xd[IPT];
     auto x_load = [&](int sb) {
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
             const int it = tid + 256 * k;
             if (it < ITEMS) {
-                const int rn = it >> 1, hf = it & 1;
+                const int rn = it >> 2, qq = it & 3;
                 const int n = min(n0 + rn, N - 1);
-                const uint32_t* p = reinterpret_cast<const uint32_t*>(X + ((int64_t)n * SB + sb) * kQ8_KBytes);
+                const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
 #pragma unroll
-                for (int d = 0; d < 32; ++d) xr[k][d] = p[1 + 32 * hf + d];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) xr[k][32 + d] = p[65 + 4 * hf + d];
-                xr[k][36] = p[0];
+                for (int d = 0; d < 4; ++d) xc[k][d] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 64 * qq + 16 * d);
+                xs[k] = *reinterpret_cast<const u32x2_a4*>(p + 260 + 8 * qq);
+                xd[k] = *reinterpret_cast<const uint32_t*>(p);
             }
         }
     };
@@ -113,21 +118,20 @@ __global__ __launch_bounds__(256) void gemm_q4k_kernel(const uint8_t* __restrict
         for (int k = 0; k < IPT; ++k) {
             const int it = tid + 256 * k;
             if (it < ITEMS) {
-                const int rn = it >> 1, hf = it & 1;
-                uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][128 * hf]);
+                const int rn = it >> 2, qq = it & 3;
+                uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][64 * qq]);
 #pragma unroll
-                for (int d = 0; d < 8; ++d)
-                    dst[d] = make_uint4(xr[k][4 * d], xr[k][4 * d + 1], xr[k][4 * d + 2], xr[k][4 * d + 3]);
-                uint32_t hs[4];
+                for (int d = 0; d < 4; ++d) dst[d] = make_uint4(xc[k][d].x, xc[k][d].y, xc[k][d].z, xc[k][d].w);
+                uint32_t hs[2];
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {  // int16 sums -> fp16 (exact: |s| <= 2032)
-                    const _Float16 lo = (_Float16)(float)(int16_t)(xr[k][32 + d] & 0xFFFF);
-                    const _Float16 hi = (_Float16)(float)(int16_t)(xr[k][32 + d] >> 16);
+                for (int d = 0; d < 2; ++d) {  // int16 sums -> fp16 (exact: |s| <= 2032)
+                    const _Float16 lo = (_Float16)(float)(int16_t)(xs[k][d] & 0xFFFF);
+                    const _Float16 hi = (_Float16)(float)(int16_t)(xs[k][d] >> 16);
                     hs[d] = (uint32_t)__builtin_bit_cast(unsigned short, lo) |
                             ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
                 }
-                reinterpret_cast<uint4*>(&s_sums[buf][rn][16 * hf])[0] = make_uint4(hs[0], hs[1], hs[2], hs[3]);
-                if (hf == 0) s_dx[buf][rn] = __uint_as_float(xr[k][36]);
+                reinterpret_cast<uint2*>(&s_sums[buf][rn][8 * qq])[0] = make_uint2(hs[0], hs[1]);
+                if (qq == 0) s_dx[buf][rn] = __uint_as_float(xd[k]);
             }
         }
     };
@@ -258,21 +262,22 @@ __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict
     const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
     const uint8_t* wrow = W + (int64_t)mrow * SB * kQ6_KBytes;
 
-    // ---- activation staging: (row, half) items of 128 codes, plus d
-    constexpr int ITEMS = BN * 2;
+    // ---- activation staging: (row, quarter) items of 64 codes, plus d
+    constexpr int ITEMS = BN * 4;
     constexpr int IPT = (ITEMS + 255) / 256;
-    uint32_t xr[IPT][33];
+    u32x4_a4 xc[IPT][4];
+    uint32_t xd[IPT];
     auto x_load = [&](int sb) {
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
             const int it = tid + 256 * k;
             if (it < ITEMS) {
-                const int rn = it >> 1, hf = it & 1;
+                const int rn = it >> 2, qq = it & 3;
                 const int n = min(n0 + rn, N - 1);
-                const uint32_t* p = reinterpret_cast<const uint32_t*>(X + ((int64_t)n * SB + sb) * kQ8_KBytes);
+                const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
 #pragma unroll
-                for (int d = 0; d < 32; ++d) xr[k][d] = p[1 + 32 * hf + d];
-                xr[k][32] = p[0];
+                for (int d = 0; d < 4; ++d) xc[k][d] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 64 * qq + 16 * d);
+                xd[k] = *reinterpret_cast<const uint32_t*>(p);
             }
         }
     };
@@ -281,12 +286,11 @@ __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict
         for (int k = 0; k < IPT; ++k) {
             const int it = tid + 256 * k;
             if (it < ITEMS) {
-                const int rn = it >> 1, hf = it & 1;
-                uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][128 * hf]);
+                const int rn = it >> 2, qq = it & 3;
+                uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][64 * qq]);
 #pragma unroll
-                for (int d = 0; d < 8; ++d)
-                    dst[d] = make_uint4(xr[k][4 * d], xr[k][4 * d + 1], xr[k][4 * d + 2], xr[k][4 * d + 3]);
-                if (hf == 0) s_dx[buf][rn] = __uint_as_float(xr[k][32]);
+                for (int d = 0; d < 4; ++d) dst[d] = make_uint4(xc[k][d].x, xc[k][d].y, xc[k][d].z, xc[k][d].w);
+                if (qq == 0) s_dx[buf][rn] = __uint_as_float(xd[k]);
             }
         }
     };
@@ -430,20 +434,10 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         }
         return hipGetLastError();
     }
-    // fewer activation rows per workgroup when the weight rows alone would
-    // not give every compute unit a workgroup
-    if (mblocks * ((N + 127) / 128) >= 256 || N <= 64) {
-        if (N <= 64) {
-            const dim3 g((unsigned)mblocks, (unsigned)((N + 63) / 64));
-            hipLaunchKernelGGL(gemm_q4k_kernel<2>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, SB);
-        } else {
-            const dim3 g((unsigned)mblocks, (unsigned)((N + 127) / 128));
-            hipLaunchKernelGGL(gemm_q4k_kernel<4>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, SB);
-        }
-    } else {
-        const dim3 g((unsigned)mblocks, (unsigned)((N + 63) / 64));
-        hipLaunchKernelGGL(gemm_q4k_kernel<2>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, SB);
-    }
+    // 64 activation rows per workgroup: two waves per SIMD fit (the 128-row
+    // tile needs one SIMD's registers per wave), measured faster at every size
+    const dim3 g((unsigned)mblocks, (unsigned)((N + 63) / 64));
+    hipLaunchKernelGGL(gemm_q4k_kernel<2>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, SB);
     return hipGetLastError();
 }
 
