@@ -66,6 +66,21 @@ __device__ __forceinline__ void order_after(long& v, const T& acc) {
 #endif
 }
 
+// XCD-aware tile order.  Workgroups are handed to the 8 XCDs round-robin
+// (workgroup i runs on XCD i % 8) and each XCD has its own L2.  Tile t is
+// (row block t / nb, column block t % nb); XCD k takes the contiguous run of
+// tiles [k * per, (k + 1) * per), so the column blocks that share a row
+// block's weights run on one XCD and read those weights into one L2, once.
+// Returns false for the workgroups past the last tile.
+__device__ __forceinline__ bool xcd_tile(int nb, int total, int& rb, int& cb) {
+    const int per = (total + 7) >> 3;
+    const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (t >= total || (int)(blockIdx.x >> 3) >= per) return false;
+    rb = t / nb;
+    cb = t - rb * nb;
+    return true;
+}
+
 constexpr int kCodeStride = 272;  // LDS bytes per activation row's 256 codes (+16: bank spread)
 constexpr int kSumStride = 32;    // LDS bytes per activation row's 16 sums as fp16
 
@@ -78,7 +93,8 @@ __device__ __forceinline__ uint32_t mul_bytes(uint32_t v, uint32_t s) {
 
 template <int NT>
 __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int N, int SB) {
+                                                       float* __restrict__ Y, int M, int N, int SB,
+                                                       int mblk, int nblk) {
     constexpr int BN = NT * 32;  // activation rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][kCodeStride];
     __shared__ __attribute__((aligned(16))) uint8_t s_sums[2][BN][kSumStride];
@@ -86,8 +102,10 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 31, h = lane >> 5;
-    const int m0 = blockIdx.x * 128 + wave * 32;
-    const int n0 = blockIdx.y * BN;
+    int rb, cb;
+    if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
+    const int m0 = rb * 128 + wave * 32;
+    const int n0 = cb * BN;
     const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
     const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
 
@@ -101,16 +119,17 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
     auto x_load = [&](int sb) {
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
-            const int it = tid + 256 * k;
-            if (it < ITEMS) {
-                const int rn = it >> 2, qq = it & 3;
-                const int n = min(n0 + rn, N - 1);
-                const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
+            // every thread loads (threads past the last item repeat an item
+            // and store nothing): no branch around a load, so the waits
+            // below retire only what they need
+            const int it = (tid + 256 * k) % ITEMS;
+            const int rn = it >> 2, qq = it & 3;
+            const int n = min(n0 + rn, N - 1);
+            const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) xc[k][d] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 64 * qq + 16 * d);
-                xs[k] = *reinterpret_cast<const u32x2_a4*>(p + 260 + 8 * qq);
-                xd[k] = *reinterpret_cast<const uint32_t*>(p);
-            }
+            for (int d = 0; d < 4; ++d) xc[k][d] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 64 * qq + 16 * d);
+            xs[k] = *reinterpret_cast<const u32x2_a4*>(p + 260 + 8 * qq);
+            xd[k] = *reinterpret_cast<const uint32_t*>(p);
         }
     };
     auto x_store = [&](int buf) {
@@ -250,15 +269,18 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
 // sub-block (any consistent assignment of k to lanes gives the same sum).
 template <int NT>
 __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int N, int SB) {
+                                                       float* __restrict__ Y, int M, int N, int SB,
+                                                       int mblk, int nblk) {
     constexpr int BN = NT * 32;
     __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][kCodeStride];
     __shared__ __attribute__((aligned(16))) float s_dx[2][BN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 31, h = lane >> 5;
-    const int m0 = blockIdx.x * 128 + wave * 32;
-    const int n0 = blockIdx.y * BN;
+    int rb, cb;
+    if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
+    const int m0 = rb * 128 + wave * 32;
+    const int n0 = cb * BN;
     const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
     const uint8_t* wrow = W + (int64_t)mrow * SB * kQ6_KBytes;
 
@@ -270,15 +292,13 @@ __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict
     auto x_load = [&](int sb) {
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
-            const int it = tid + 256 * k;
-            if (it < ITEMS) {
-                const int rn = it >> 2, qq = it & 3;
-                const int n = min(n0 + rn, N - 1);
-                const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
+            const int it = (tid + 256 * k) % ITEMS;  // unconditional, as for Q4_K
+            const int rn = it >> 2, qq = it & 3;
+            const int n = min(n0 + rn, N - 1);
+            const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) xc[k][d] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 64 * qq + 16 * d);
-                xd[k] = *reinterpret_cast<const uint32_t*>(p);
-            }
+            for (int d = 0; d < 4; ++d) xc[k][d] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 64 * qq + 16 * d);
+            xd[k] = *reinterpret_cast<const uint32_t*>(p);
         }
     };
     auto x_store = [&](int buf) {
@@ -422,22 +442,29 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
     const uint8_t* w = static_cast<const uint8_t*>(W);
     const uint8_t* x = static_cast<const uint8_t*>(xq);
     const int64_t mblocks = (M + 127) / 128;
+    // one workgroup of 256 threads per tile; the whole grid must stay within
+    // 2^32 work-items
+    const int64_t tiles_max = (int64_t)mblocks * ((N + 63) / 64);
+    if (8 * ((tiles_max + 7) / 8) * 256 > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+    auto grid = [](int64_t tiles) { return dim3((unsigned)(8 * ((tiles + 7) / 8))); };
     if (wtype == QMM_Q6_K) {
         // bound by streaming W: one 32-row activation tile per workgroup up to
         // N = 32 (W read once), wider tiles beyond
         if (N <= 32) {
-            hipLaunchKernelGGL(gemm_q6k_kernel<1>, dim3((unsigned)mblocks, 1), dim3(256), 0, s, w, x, y, (int)M,
-                               (int)N, SB);
+            hipLaunchKernelGGL(gemm_q6k_kernel<1>, grid(mblocks), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
+                               (int)mblocks, 1);
         } else {
-            hipLaunchKernelGGL(gemm_q6k_kernel<2>, dim3((unsigned)mblocks, (unsigned)((N + 63) / 64)), dim3(256), 0,
-                               s, w, x, y, (int)M, (int)N, SB);
+            const int64_t nb = (N + 63) / 64;
+            hipLaunchKernelGGL(gemm_q6k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
+                               (int)mblocks, (int)nb);
         }
         return hipGetLastError();
     }
     // 64 activation rows per workgroup: two waves per SIMD fit (the 128-row
     // tile needs one SIMD's registers per wave), measured faster at every size
-    const dim3 g((unsigned)mblocks, (unsigned)((N + 63) / 64));
-    hipLaunchKernelGGL(gemm_q4k_kernel<2>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, SB);
+    const int64_t nb = (N + 63) / 64;
+    hipLaunchKernelGGL(gemm_q4k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
+                       (int)mblocks, (int)nb);
     return hipGetLastError();
 }
 
