@@ -54,6 +54,7 @@ typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Makes `v` depend on `acc`, so that the matrix instruction consuming `v` is
@@ -91,16 +92,33 @@ __device__ __forceinline__ uint32_t mul_bytes(uint32_t v, uint32_t s) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Activation tile of one super-block in LDS: column n's 256 codes at
+// codes[n] (row stride kCodeStride spreads the operand reads over the LDS
+// banks), its 16 sums, its scale.
+template <int BN>
+struct XTile {
+    uint8_t codes[BN][kCodeStride];
+    int16_t sums[BN][16];
+    float dx[BN];
+};
+
+// The activation tile is copied from global memory straight into LDS
+// (buffer_load ... lds: no VGPR round trip, no VALU), one super-block
+// ahead.  The two tiles are distinct LDS objects, so the compiler can see
+// that reading one tile never waits for the copy into the other; the
+// barrier that ends each super-block waits for the copy.  The buffer descriptor covers only this workgroup's
+// activation rows: rows past N read as zeros (their outputs are not stored).
 template <int NT>
 __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
                                                        float* __restrict__ Y, int M, int N, int SB,
                                                        int mblk, int nblk) {
     constexpr int BN = NT * 32;  // activation rows per workgroup
-    __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][kCodeStride];
-    __shared__ __attribute__((aligned(16))) uint8_t s_sums[2][BN][kSumStride];
-    __shared__ __attribute__((aligned(16))) float s_dx[2][BN];
+    static_assert(BN % 32 == 0 && BN <= 64, "staging assumes 4 waves and at most 64 rows");
+    __shared__ __attribute__((aligned(16))) XTile<BN> tile0;
+    __shared__ __attribute__((aligned(16))) XTile<BN> tile1;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave-uniform (scalar) wave index: the copies' LDS addresses go to M0
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, h = lane >> 5;
     int rb, cb;
     if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
@@ -109,50 +127,28 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
     const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
     const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
 
-    // ---- activation staging: every thread owns (row, quarter) items: 64
-    //      codes, their 4 sums, and (quarter 0) the scale; 16-byte loads
-    constexpr int ITEMS = BN * 4;
-    constexpr int IPT = (ITEMS + 255) / 256;
-    u32x4_a4 xc[IPT][4];
-    u32x2_a4 xs[IPT];
-    uint32_t xd[IPT];
-    auto x_load = [&](int sb) {
+    // ---- activation copies (per lane: constant offsets; per super-block: scalar offsets)
+    const int rowsB = SB * kQ8_KBytes;  // bytes of one activation row
+    const int nrows = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(X) + (int64_t)n0 * rowsB, (short)0, nrows * rowsB, kBufferWord3);
+    const unsigned vo_codes = 4u + 4u * lane;                                   // dword l of the 256 codes
+    const unsigned vo_sums = (unsigned)((lane >> 3) * rowsB + 260 + 4 * (lane & 7));  // 8 rows x 8 dwords
+    const unsigned vo_dx = (unsigned)(lane * rowsB);                            // row l's scale
+    auto x_copy = [&](XTile<BN>& T, int sb) {
+        const int sbB = sb * kQ8_KBytes;
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            // every thread loads (threads past the last item repeat an item
-            // and store nothing): no branch around a load, so the waits
-            // below retire only what they need
-            const int it = (tid + 256 * k) % ITEMS;
-            const int rn = it >> 2, qq = it & 3;
-            const int n = min(n0 + rn, N - 1);
-            const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) xc[k][d] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 64 * qq + 16 * d);
-            xs[k] = *reinterpret_cast<const u32x2_a4*>(p + 260 + 8 * qq);
-            xd[k] = *reinterpret_cast<const uint32_t*>(p);
+        for (int i = 0; i < BN / 4; ++i) {  // rows wave, wave + 4, ...: one instruction per row
+            const int n = wave + 4 * i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.codes[n][0], 4, vo_codes, (unsigned)(n * rowsB + sbB), 0, 0);
         }
-    };
-    auto x_store = [&](int buf) {
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int it = tid + 256 * k;
-            if (it < ITEMS) {
-                const int rn = it >> 2, qq = it & 3;
-                uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][64 * qq]);
-#pragma unroll
-                for (int d = 0; d < 4; ++d) dst[d] = make_uint4(xc[k][d].x, xc[k][d].y, xc[k][d].z, xc[k][d].w);
-                uint32_t hs[2];
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {  // int16 sums -> fp16 (exact: |s| <= 2032)
-                    const _Float16 lo = (_Float16)(float)(int16_t)(xs[k][d] & 0xFFFF);
-                    const _Float16 hi = (_Float16)(float)(int16_t)(xs[k][d] >> 16);
-                    hs[d] = (uint32_t)__builtin_bit_cast(unsigned short, lo) |
-                            ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
-                }
-                reinterpret_cast<uint2*>(&s_sums[buf][rn][8 * qq])[0] = make_uint2(hs[0], hs[1]);
-                if (qq == 0) s_dx[buf][rn] = __uint_as_float(xd[k]);
-            }
+        for (int i = 0; i < BN / 32; ++i) {  // sums of rows 8g .. 8g+7 per instruction
+            const int g = wave + 4 * i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.sums[8 * g][0], 4, vo_sums, (unsigned)(8 * g * rowsB + sbB), 0, 0);
         }
+        if (wave == 0 && lane < BN)  // (BN < 64: the other lanes' copies would fall past the tile)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.dx[0], 4, vo_dx, (unsigned)sbB, 0, 0);
     };
     // ---- weights: header + this lane's halves of the four nibble-pair chunks
     uint4 wh, wq[4];
@@ -169,37 +165,20 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
 #pragma unroll
         for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
 
-    x_load(0);
-    w_load(0, wh, wq);
-    x_store(0);
-    __syncthreads();
-
-    for (int sb = 0; sb < SB; ++sb) {
-        const int buf = sb & 1;
+    // one super-block: T is this super-block's tile, Tn receives the next one
+    auto step = [&](const int sb, XTile<BN>& T, XTile<BN>& Tn) {
         const uint4 hdr = wh;
         uint4 q[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) q[g] = wq[g];
         if (sb + 1 < SB) {
-            x_load(sb + 1);
+            x_copy(Tn, sb + 1);
             w_load(sb + 1, wh, wq);
         }
         const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
         const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
         const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
         const uint32_t m47 = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
-
-        // min term: lane K half h covers 16-wide sums 8h..8h+7, i.e. mins 4h..4h+3 twice each
-        const uint32_t mw = h ? m47 : m03;
-        v8h mins;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mins[e] = (_Float16)(float)((mw >> (8 * (e >> 1))) & 0xFF);
-        v16f amin[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const v8h bs = *reinterpret_cast<const v8h*>(&s_sums[buf][32 * t + c][16 * h]);
-            amin[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bs, mins, (v16f){}, 0, 0, 0);
-        }
 
         v16i ahi[NT], alo[NT];
 #pragma unroll
@@ -222,29 +201,49 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
                             (int)mul_bytes(q3, sl)};
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const v4i a = *reinterpret_cast<const v4i*>(&s_codes[buf][32 * t + c][32 * j + 16 * h]);
+                const v4i a = *reinterpret_cast<const v4i*>(&T.codes[32 * t + c][32 * j + 16 * h]);
                 ahi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bh, ahi[t], 0, 0, 0);
                 alo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bl, alo[t], 0, 0, 0);
             }
         }
+        // min term (its tile is live only in the epilogue): lane K half h
+        // covers 16-wide sums 8h..8h+7, i.e. mins 4h..4h+3 twice each
+        const uint32_t mw = h ? m47 : m03;
+        v8h mins;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mins[e] = (_Float16)(float)((mw >> (8 * (e >> 1))) & 0xFF);
         // epilogue: y[n][m] += dx_n * (d * (8 P_hi + P_lo) - dmin * Smin)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+            const v8s bi = *reinterpret_cast<const v8s*>(&T.sums[32 * t + c][8 * h]);
+            v8h bs;  // int16 sums -> fp16 (exact: |s| <= 2032)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bs[e] = (_Float16)bi[e];
+            const v16f amin = __builtin_amdgcn_mfma_f32_32x32x16_f16(bs, mins, (v16f){}, 0, 0, 0);
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const float4 dx = *reinterpret_cast<const float4*>(&s_dx[buf][32 * t + 8 * qd + 4 * h]);
+                const float4 dx = *reinterpret_cast<const float4*>(&T.dx[32 * t + 8 * qd + 4 * h]);
                 const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * qd + e;
                     const int u = ahi[t][r] * 8 + alo[t][r];
-                    const float v = (float)u * d - dmin * amin[t][r];
+                    const float v = (float)u * d - dmin * amin[r];
                     yacc[t][r] += v * dxa[e];
                 }
             }
         }
-        if (sb + 1 < SB) x_store(buf ^ 1);
-        __syncthreads();
+        __syncthreads();  // the next tile has landed (waits for the copies) and this one is free
+    };
+
+    x_copy(tile0, 0);
+    w_load(0, wh, wq);
+    __syncthreads();
+    // (each arm names its tiles statically, which is what lets the compiler
+    // tell the two apart)
+    for (int sb = 0; sb < SB; ++sb) {
+        if (sb & 1) step(sb, tile1, tile0);
+        else step(sb, tile0, tile1);
     }
 
     const int m = m0 + c;
