@@ -89,6 +89,12 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
 // for x - loads retire in order - does not wait for W).  The activation rows
 // are contiguous, so item i's bytes follow item i-1's.
 
+template <bool First, int Lanes>
+struct RoundTag {
+    static constexpr bool first = First;
+    static constexpr int lanes = Lanes;
+};
+
 template <int WT, int NC, bool XF, class Hook>
 __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, Hook&& after_loads) {
     constexpr bool kQ80 = (WT == QMM_Q4_0 || WT == QMM_Q8_0);
@@ -102,43 +108,62 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
     // does not wait for the W prefetch issued after it.
     const int wave0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x) & ~63;  // first thread of this wave
     auto round = [&](const int base, auto first) {
-        constexpr bool kFirst = decltype(first)::value;
+        constexpr bool kFirst = decltype(first)::first;
         if constexpr (XF && kQ80) {
-            // fp32 rows quantized here to Q8_0, exactly as the stand-alone
-            // quantizer does: item i = values 32i .. 32i+31.
-            const int i = base + threadIdx.x;
+            // fp32 rows quantized here to Q8_0 by S adjacent lanes per
+            // 32-value block (each lane 32/S values; the block maximum and
+            // the code sum are combined through shuffles), exactly as the
+            // stand-alone quantizer does.  S is chosen by stage_x below.
+            constexpr int S = decltype(first)::lanes;
+            constexpr int NF = 8 / S;  // float4 per lane
+            const int slot = (int)threadIdx.x / S, si = (int)threadIdx.x % S;
+            const int i = base + slot;
             const int ic = i < nitems ? i : nitems - 1;
-            float4 v[8];
-            if (base + wave0 < nitems) {
+            float4 v[NF];
+            if (base + wave0 / S < nitems) {
 #pragma unroll
-                for (int h = 0; h < 8; ++h) v[h] = reinterpret_cast<const float4*>(xq)[8 * ic + h];
+                for (int h = 0; h < NF; ++h) v[h] = reinterpret_cast<const float4*>(xq)[8 * ic + NF * si + h];
             }
             if constexpr (kFirst) {
-                __builtin_amdgcn_sched_barrier(0);  // keep x's loads ahead of W's (loads retire in order)
+                // Every wave of the workgroup issues its x loads before any
+                // wave issues W loads: the memory pipeline serves a compute
+                // unit's requests in order, and x (needed first, by every
+                // wave) would otherwise queue behind other waves' W traffic.
+                // The barrier waits for no data.
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
                 after_loads();
             }
+            float amax = 0.0f;
+#pragma unroll
+            for (int h = 0; h < NF; ++h)
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[h].x), fabsf(v[h].y)), fmaxf(fabsf(v[h].z), fabsf(v[h].w))));
+#pragma unroll
+            for (int o = 1; o < S; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+            float d, id;
+            rtn_scale(amax, d, id);
+            uint32_t q[NF];
+            int sx = 0;
+#pragma unroll
+            for (int h = 0; h < NF; ++h) {
+                q[h] = (uint32_t)(rtn_code(v[h].x * id) & 0xFF) | ((uint32_t)(rtn_code(v[h].y * id) & 0xFF) << 8) |
+                       ((uint32_t)(rtn_code(v[h].z * id) & 0xFF) << 16) |
+                       ((uint32_t)(rtn_code(v[h].w * id) & 0xFF) << 24);
+                sx = dot4(q[h], 0x01010101u, sx);
+            }
+#pragma unroll
+            for (int o = 1; o < S; o <<= 1) sx += __shfl_xor(sx, o);
             if (i < nitems) {
-                float amax = 0.0f;
-#pragma unroll
-                for (int h = 0; h < 8; ++h)
-                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[h].x), fabsf(v[h].y)), fmaxf(fabsf(v[h].z), fabsf(v[h].w))));
-                float d, id;
-                rtn_scale(amax, d, id);
-                uint32_t q[8];
-                int sx = 0;
-#pragma unroll
-                for (int h = 0; h < 8; ++h) {
-                    q[h] = (uint32_t)(rtn_code(v[h].x * id) & 0xFF) | ((uint32_t)(rtn_code(v[h].y * id) & 0xFF) << 8) |
-                           ((uint32_t)(rtn_code(v[h].z * id) & 0xFF) << 16) |
-                           ((uint32_t)(rtn_code(v[h].w * id) & 0xFF) << 24);
-                    sx = dot4(q[h], 0x01010101u, sx);
-                }
                 uint8_t* rec = xl + (i >> 3) * XREC;
                 const int bi = i & 7;
-                reinterpret_cast<uint4*>(rec + 32 * bi)[0] = make_uint4(q[0], q[1], q[2], q[3]);
-                reinterpret_cast<uint4*>(rec + 32 * bi)[1] = make_uint4(q[4], q[5], q[6], q[7]);
-                reinterpret_cast<float*>(rec)[64 + bi] = h2f(f2h(d));  // the block stores fp16(d)
-                reinterpret_cast<int*>(rec)[72 + bi] = 8 * sx;
+                uint32_t* dst = reinterpret_cast<uint32_t*>(rec + 32 * bi) + NF * si;
+#pragma unroll
+                for (int h = 0; h < NF; ++h) dst[h] = q[h];
+                if (si == 0) {
+                    reinterpret_cast<float*>(rec)[64 + bi] = h2f(f2h(d));  // the block stores fp16(d)
+                    reinterpret_cast<int*>(rec)[72 + bi] = 8 * sx;
+                }
             }
         } else if constexpr (XF) {
             // fp32 rows quantized here to Q8_K: item i = quarter i&3 of block
@@ -153,7 +178,14 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
                 for (int h = 0; h < 16; ++h) v[h] = reinterpret_cast<const float4*>(xq)[16 * ic + h];
             }
             if constexpr (kFirst) {
-                __builtin_amdgcn_sched_barrier(0);  // keep x's loads ahead of W's (loads retire in order)
+                // Every wave of the workgroup issues its x loads before any
+                // wave issues W loads: the memory pipeline serves a compute
+                // unit's requests in order, and x (needed first, by every
+                // wave) would otherwise queue behind other waves' W traffic.
+                // The barrier waits for no data.
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
                 after_loads();
             }
             if (i < nitems) {
@@ -207,7 +239,14 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
                 }
             }
             if constexpr (kFirst) {
-                __builtin_amdgcn_sched_barrier(0);  // keep x's loads ahead of W's (loads retire in order)
+                // Every wave of the workgroup issues its x loads before any
+                // wave issues W loads: the memory pipeline serves a compute
+                // unit's requests in order, and x (needed first, by every
+                // wave) would otherwise queue behind other waves' W traffic.
+                // The barrier waits for no data.
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
                 after_loads();
             }
 #pragma unroll
@@ -246,7 +285,14 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
                 }
             }
             if constexpr (kFirst) {
-                __builtin_amdgcn_sched_barrier(0);  // keep x's loads ahead of W's (loads retire in order)
+                // Every wave of the workgroup issues its x loads before any
+                // wave issues W loads: the memory pipeline serves a compute
+                // unit's requests in order, and x (needed first, by every
+                // wave) would otherwise queue behind other waves' W traffic.
+                // The barrier waits for no data.
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
                 after_loads();
             }
 #pragma unroll
@@ -276,8 +322,17 @@ __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, H
             }
         }
     };
-    round(0, std::true_type{});
-    for (int base = step; base < nitems; base += step) round(base, std::false_type{});
+    if constexpr (XF && kQ80) {
+        // lanes per block: as many as the workgroup has to spare, up to 8
+        const int spare = (int)blockDim.x / nitems;
+        if (spare >= 8) round(0, RoundTag<true, 8>{});
+        else if (spare >= 4) round(0, RoundTag<true, 4>{});
+        else if (spare >= 2) round(0, RoundTag<true, 2>{});
+        else round(0, RoundTag<true, 1>{});
+    } else {
+        round(0, RoundTag<true, 1>{});
+    }
+    for (int base = step; base < nitems; base += step) round(base, RoundTag<false, 1>{});
 }
 
 // ------------------------------------------------------- unit compute
@@ -785,9 +840,13 @@ hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const i
     for (int i = nseg; i < kMaxSeg; ++i) a.seg[i] = a.seg[0];
     a.nwork = work;
     const int64_t xrowB = xf32 ? K * 4 : (int64_t)a.G * (WT == QMM_Q4_0 || WT == QMM_Q8_0 ? 8 * kQ8_0Bytes : kQ8_KBytes);
-    // waves per workgroup: spread small problems over all CUs
+    // waves per workgroup: spread small problems over all CUs.  A launch that
+    // quantizes x itself uses 2 to 4 waves: enough lanes to share each
+    // block's quantization, few enough that one compute unit's W requests do
+    // not hold up the x loads of its later waves (measured on the 1B-Llama
+    // decode shapes).
     const int64_t per_cu = (work + di.cus - 1) / di.cus;
-    const int wpg = per_cu >= 8 ? 8 : per_cu >= 4 ? 4 : per_cu >= 2 ? 2 : 1;
+    const int wpg = xf32 ? (per_cu >= 4 ? 4 : 2) : per_cu >= 8 ? 8 : per_cu >= 4 ? 4 : per_cu >= 2 ? 2 : 1;
     for (int64_t n0 = 0; n0 < N;) {
         int nc = (int)(N - n0 < 8 ? N - n0 : 8);
         while (nc > 1 && (size_t)nc * a.G * XREC > di.lds) --nc;
