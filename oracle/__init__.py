@@ -24,11 +24,11 @@ _SRC = os.path.join(_HERE, "qmm_oracle.c")
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 # Oracle type codes (its own).
-Q4_0, Q8_0, Q4_K, Q6_K, Q8_K = 1, 2, 3, 4, 5
-TYPE_NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q8_K: "Q8_K"}
-BLOCK_SIZE = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256, Q8_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210, Q8_K: 292}
-VEC_DOT_TYPE = {Q4_0: Q8_0, Q8_0: Q8_0, Q4_K: Q8_K, Q6_K: Q8_K}
+Q4_0, Q8_0, Q4_K, Q6_K, Q8_K, Q5_0 = 1, 2, 3, 4, 5, 6
+TYPE_NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q8_K: "Q8_K", Q5_0: "Q5_0"}
+BLOCK_SIZE = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256, Q8_K: 256, Q5_0: 32}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210, Q8_K: 292, Q5_0: 22}
+VEC_DOT_TYPE = {Q4_0: Q8_0, Q8_0: Q8_0, Q4_K: Q8_K, Q6_K: Q8_K, Q5_0: Q8_0}
 
 CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
           "-Wall", "-Wextra", "-shared", "-fPIC"]
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         L.orc_q6k_quant.restype = I
         L.orc_q4k_scale_min_n.argtypes = [P, I64, P, P]
         L.orc_q6k_quant_n.argtypes = [P, I64, P]
+        L.orc_q5_0_quant_n.argtypes = [P, I64, P]
         L.orc_num_threads.restype = I
         _lib = L
     return _lib
@@ -180,6 +181,14 @@ def q6k_quant_n(blocks: np.ndarray) -> np.ndarray:
     b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1, 210)
     q = np.empty((b.shape[0], 256), np.uint8)
     lib().orc_q6k_quant_n(_ptr(b), b.shape[0], _ptr(q))
+    return q
+
+
+def q5_0_quant_n(blocks: np.ndarray) -> np.ndarray:
+    """Unsigned 5-bit quants of n Q5_0 blocks -> (n, 32) uint8."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1, 22)
+    q = np.empty((b.shape[0], 32), np.uint8)
+    lib().orc_q5_0_quant_n(_ptr(b), b.shape[0], _ptr(q))
     return q
 
 

@@ -1,6 +1,6 @@
 /*
  * qmm_oracle.c — plain CPU oracle for the GGUF block-quantized matrix
- * product (Q4_0, Q8_0, Q4_K, Q6_K weights; Q8_0 and Q8_K activations).
+ * product (Q4_0, Q5_0, Q8_0, Q4_K, Q6_K weights; Q8_0 and Q8_K activations).
  *
  * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg load this library.  It shares no code with the GPU path.
@@ -8,6 +8,8 @@
  * What it follows (page "The GGML ecosystem, and where synapse fits", §5
  * "Quantization"):
  *   - the format table: Q4_0 = fp16 d + 32 four-bit quants, w = d(q-8), 18 B;
+ *     Q5_0 = fp16 d + a 32-bit word of fifth bits + 32 four-bit low parts,
+ *     w = d(q-16), 22 B;
  *     Q8_0 = fp16 d + 32 int8, w = d q, 34 B; Q4_K = fp16 d, dmin, eight
  *     32-wide sub-blocks with a 6-bit scale and a 6-bit min each,
  *     w = d sc q - dmin m, 144 B; Q6_K = fp16 d, sixteen 16-wide sub-blocks
@@ -43,7 +45,7 @@
 
 int orc_block_size(int type) {
     switch (type) {
-    case ORC_Q4_0: case ORC_Q8_0: return 32;
+    case ORC_Q4_0: case ORC_Q5_0: case ORC_Q8_0: return 32;
     case ORC_Q4_K: case ORC_Q6_K: case ORC_Q8_K: return 256;
     default: return 0;
     }
@@ -52,6 +54,7 @@ int orc_block_size(int type) {
 size_t orc_block_bytes(int type) {
     switch (type) {
     case ORC_Q4_0: return 18;   /* 2 (d) + 16 (32 nibbles)                   */
+    case ORC_Q5_0: return 22;   /* 2 (d) + 4 (32 fifth bits) + 16 (nibbles)  */
     case ORC_Q8_0: return 34;   /* 2 (d) + 32 (int8)                         */
     case ORC_Q4_K: return 144;  /* 2 (d) + 2 (dmin) + 12 (scales) + 128 (qs) */
     case ORC_Q6_K: return 210;  /* 128 (ql) + 64 (qh) + 16 (scales) + 2 (d)  */
@@ -216,6 +219,9 @@ int orc_quantize_q4_0(const float* x, void* out, int64_t rows, int64_t K) {
 /* GGUF arrangements (the reading taken; little-endian multi-byte fields):
  *  Q4_0 [d:2][qs:16]        element e<16 = low nibble of qs[e],
  *                           e>=16 = high nibble of qs[e-16]
+ *  Q5_0 [d:2][qh:4][qs:16]  low four bits as Q4_0's nibbles (in qs),
+ *                           fifth bit of element e = bit e of the
+ *                           little-endian 32-bit qh
  *  Q8_0 [d:2][qs:32 int8]
  *  Q4_K [d:2][dmin:2][scales:12][qs:128]  sub-block j = e/32 uses the
  *        32 bytes qs[32(j/2) ...], low nibbles for even j, high for odd j
@@ -225,6 +231,18 @@ int orc_quantize_q4_0(const float* x, void* out, int64_t rows, int64_t K) {
 static int q4_0_quant(const uint8_t* blk, int e) {
     const uint8_t* qs = blk + 2;
     return e < 16 ? (qs[e] & 0xF) : (qs[e - 16] >> 4);
+}
+
+static int q5_0_quant(const uint8_t* blk, int e) {
+    const uint8_t* qs = blk + 6;
+    uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) | ((uint32_t)blk[5] << 24);
+    int lo = e < 16 ? (qs[e] & 0xF) : (qs[e - 16] >> 4);
+    return lo | (int)(((qh >> e) & 1u) << 4);
+}
+
+void orc_q5_0_quant_n(const uint8_t* blocks, int64_t n, uint8_t* q) {
+    for (int64_t i = 0; i < n; ++i)
+        for (int e = 0; e < 32; ++e) q[32 * i + e] = (uint8_t)q5_0_quant(blocks + 22 * i, e);
 }
 
 /* The 12 scale bytes hold eight 6-bit scales and eight 6-bit mins.  Bytes
@@ -281,6 +299,7 @@ void orc_q6k_quant_n(const uint8_t* blocks, int64_t n, uint8_t* q) {
 
 /* fp32 dequantizer.  Order of operations per element (all fp32):
  *   Q4_0: d * (float)(q - 8)          Q8_0: d * (float)q
+ *   Q5_0: d * (float)(q - 16)
  *   Q4_K: (d * sc) * q - (dmin * m)   Q6_K: (d * sc) * (float)(q - 32)
  *   Q8_K: d * (float)q
  * Every product above is exact in fp32 except Q8_K's, so the only roundings
@@ -298,6 +317,10 @@ int orc_dequantize_f32(int type, const void* blocks, float* out, int64_t rows, i
         case ORC_Q4_0: {
             float d = rd_fp16(blk);
             for (int e = 0; e < 32; ++e) o[e] = d * (float)(q4_0_quant(blk, e) - 8);
+        } break;
+        case ORC_Q5_0: {
+            float d = rd_fp16(blk);
+            for (int e = 0; e < 32; ++e) o[e] = d * (float)(q5_0_quant(blk, e) - 16);
         } break;
         case ORC_Q8_0: {
             float d = rd_fp16(blk);
@@ -339,6 +362,10 @@ static void deq_block_f64(int type, const uint8_t* blk, double* o) {
         double d = rd_fp16(blk);
         for (int e = 0; e < 32; ++e) o[e] = d * (q4_0_quant(blk, e) - 8);
     } break;
+    case ORC_Q5_0: {
+        double d = rd_fp16(blk);
+        for (int e = 0; e < 32; ++e) o[e] = d * (q5_0_quant(blk, e) - 16);
+    } break;
     case ORC_Q8_0: {
         double d = rd_fp16(blk);
         for (int e = 0; e < 32; ++e) o[e] = d * (int8_t)blk[2 + e];
@@ -377,7 +404,7 @@ int orc_dequantize_f64(int type, const void* blocks, double* out, int64_t rows, 
 
 static int vec_dot_type(int wtype) {
     switch (wtype) {
-    case ORC_Q4_0: case ORC_Q8_0: return ORC_Q8_0;
+    case ORC_Q4_0: case ORC_Q5_0: case ORC_Q8_0: return ORC_Q8_0;
     case ORC_Q4_K: case ORC_Q6_K: return ORC_Q8_K;
     default: return 0;
     }
@@ -458,10 +485,11 @@ int orc_mul_mat_blockwise(int wtype, const void* W, const void* xq, double* y,
             for (int64_t b = 0; b < nbw; ++b) {
                 const uint8_t* wb = wrow + b * SW;
                 const uint8_t* xb = xrow + b * SX; /* same block size on both sides */
-                if (wtype == ORC_Q8_0 || wtype == ORC_Q4_0) {
+                if (wtype == ORC_Q8_0 || wtype == ORC_Q4_0 || wtype == ORC_Q5_0) {
                     int64_t isum = 0;
                     for (int e = 0; e < 32; ++e) {
-                        int qw = (wtype == ORC_Q8_0) ? (int8_t)wb[2 + e] : q4_0_quant(wb, e) - 8;
+                        int qw = (wtype == ORC_Q8_0) ? (int8_t)wb[2 + e]
+                               : (wtype == ORC_Q4_0) ? q4_0_quant(wb, e) - 8 : q5_0_quant(wb, e) - 16;
                         isum += (int64_t)qw * (int8_t)xb[2 + e];
                     }
                     acc += (double)rd_fp16(wb) * (double)rd_fp16(xb) * (double)isum;

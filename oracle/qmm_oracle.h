@@ -37,7 +37,7 @@ extern "C" {
 
 /* Oracle type codes (its own; numerically equal to the library's by choice
  * of both, not by a shared header). */
-enum { ORC_Q4_0 = 1, ORC_Q8_0 = 2, ORC_Q4_K = 3, ORC_Q6_K = 4, ORC_Q8_K = 5 };
+enum { ORC_Q4_0 = 1, ORC_Q8_0 = 2, ORC_Q4_K = 3, ORC_Q6_K = 4, ORC_Q8_K = 5, ORC_Q5_0 = 6 };
 
 int    orc_block_size(int type);   /* values per block; 0 if unknown */
 size_t orc_block_bytes(int type);  /* bytes per block; 0 if unknown  */
@@ -95,6 +95,8 @@ int  orc_q6k_quant(const uint8_t* block210, int e); /* unsigned 6-bit q of eleme
  * n Q6_K blocks -> n x 256 unsigned quants. */
 void orc_q4k_scale_min_n(const uint8_t* scales12, int64_t n, int32_t* sc, int32_t* m);
 void orc_q6k_quant_n(const uint8_t* blocks, int64_t n, uint8_t* q);
+/* n Q5_0 blocks -> n x 32 unsigned 5-bit quants. */
+void orc_q5_0_quant_n(const uint8_t* blocks, int64_t n, uint8_t* q);
 
 /* Threads the OpenMP runtime will use (for the CPU baseline report). */
 int orc_num_threads(void);

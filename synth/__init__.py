@@ -62,6 +62,23 @@ def q6_k_random(g: np.random.Generator, rows: int, K: int) -> np.ndarray:
     return blk.reshape(rows, nb * Q6_K_BYTES)
 
 
+def q5_0_random(g: np.random.Generator, rows: int, K: int) -> np.ndarray:
+    """(rows, K/32*22) uint8 of random raw Q5_0 blocks: uniform fifth-bit
+    words and nibbles, d = fp16(|N(0, 1e-3)|) as for the K-quant workloads."""
+    assert K % 32 == 0
+    nb = K // 32
+    blk = g.integers(0, 256, size=(rows, nb, 22), dtype=np.uint8)
+    blk[:, :, 0:2] = _abs_normal_fp16_bytes(g, (rows, nb), 1e-3)
+    return blk.reshape(rows, nb * 22)
+
+
+# Qwen2.5-0.5B-shaped layer: 896-wide rows are not a multiple of 256, so a
+# K-quant mix stores them as Q5_0 (page "The GGML ecosystem, and where synapse
+# fits", §3, the fallback rule); ffn_down's 4864-wide rows are.
+QWEN_0_5B_Q5_0 = (("attn_q", 896, 896), ("attn_k", 128, 896), ("attn_v", 128, 896),
+                  ("attn_output", 896, 896), ("ffn_gate", 4864, 896), ("ffn_up", 4864, 896))
+
+
 def uniform_bytes(g: np.random.Generator, shape) -> np.ndarray:
     return g.integers(0, 256, size=shape, dtype=np.uint8)
 
@@ -78,3 +95,9 @@ LLAMA_1B_LAYER = (
 LLAMA_1B_LAYERS = 16
 LLAMA_8B_SHAPES = ((4096, 4096), (14336, 4096), (4096, 14336))
 LLAMA_8B_HEAD = (128256, 4096)
+
+# KV cache of the 8B GQA model ("llama.cpp and GGUF", KV memory: 2 x L x n_kv x
+# d_h values per token): 32 layers, 8 KV heads of 128 -> one K row and one V
+# row of 1024 values per token and layer.
+LLAMA_8B_KV = {"layers": 32, "kv_heads": 8, "head_dim": 128}
+LLAMA_8B_KV_ROW = LLAMA_8B_KV["kv_heads"] * LLAMA_8B_KV["head_dim"]

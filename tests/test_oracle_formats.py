@@ -17,7 +17,7 @@ import pytest
 
 import oracle as O
 
-NAMES = {"Q4_0": O.Q4_0, "Q8_0": O.Q8_0, "Q4_K": O.Q4_K, "Q6_K": O.Q6_K, "Q8_K": O.Q8_K}
+NAMES = {"Q4_0": O.Q4_0, "Q8_0": O.Q8_0, "Q4_K": O.Q4_K, "Q6_K": O.Q6_K, "Q8_K": O.Q8_K, "Q5_0": O.Q5_0}
 
 
 def fp16_bytes(bits):
@@ -37,6 +37,7 @@ def test_format_table_sizes(golden):
     bpw = {n: 8 * f["block_bytes"] / f["block_size"] for n, f in g["formats"].items()}
     assert bpw["Q4_K"] == g["bits_per_weight"]["Q4_K"]
     assert bpw["Q4_0"] == 4.5
+    assert bpw["Q5_0"] == 5.5   # 2 + 4 + 16 bytes per 32
     assert abs(bpw["Q8_0"] - g["bits_per_weight"]["Q8_0"]) < 1e-12
     lo, hi = g["k_quant_bpw_range"]
     assert lo <= bpw["Q6_K"] <= hi and lo <= bpw["Q4_K"] <= hi
@@ -60,6 +61,25 @@ def test_hand_q4_0(golden):
     y, T = O.mul_mat(O.Q4_0, blk, x, 1, 1, 32)
     assert y[0, 0] == h["dot_with_q8_0_d1_all_ones"]
     assert O.mul_mat_blockwise(O.Q4_0, blk, x, 1, 1, 32)[0, 0] == h["dot_with_q8_0_d1_all_ones"]
+    assert T[0, 0] == sum(abs(v) for v in h["w"])
+
+
+@pytest.mark.parametrize("which", ["a", "b"])
+def test_hand_q5_0(golden, which):
+    h = golden("hand_blocks.json")["q5_0"][which]
+    blk = np.zeros(22, np.uint8)
+    blk[0:2] = fp16_bytes(h["d_fp16_bits"])
+    blk[2:6] = np.array([h["qh"]], "<u4").view(np.uint8)
+    if h["qs_rule"] == "qs[j] = 0x80 | j":
+        blk[6:22] = 0x80 | np.arange(16)
+    w = O.dequantize(O.Q5_0, blk, 1, 32)[0]
+    assert w.tolist() == h["w"]
+    x = np.zeros(34, np.uint8)
+    x[0:2] = fp16_bytes(0x3C00)
+    x[2:] = 1
+    y, T = O.mul_mat(O.Q5_0, blk, x, 1, 1, 32)
+    assert y[0, 0] == h["dot_with_q8_0_d1_all_ones"]
+    assert O.mul_mat_blockwise(O.Q5_0, blk, x, 1, 1, 32)[0, 0] == h["dot_with_q8_0_d1_all_ones"]
     assert T[0, 0] == sum(abs(v) for v in h["w"])
 
 
@@ -252,9 +272,29 @@ def test_q4_0_bits():
     _flip_test(decode, 16, lambda bit: ((bit // 8) + (16 if bit % 8 >= 4 else 0), bit % 4))
 
 
+def test_q5_0_bits():
+    # qh bit e moves element e by 16; qs bit b of byte j moves element j
+    # (b < 4) or j + 16 (b >= 4) by 2^(b % 4); the scale bytes are left alone
+    def decode(raw):
+        n = raw.shape[0]
+        blk = np.zeros((n, 22), np.uint8)
+        blk[:, 0:2] = fp16_bytes(0x3C00)
+        blk[:, 2:] = raw
+        return O.dequantize(O.Q5_0, blk, n, 32).astype(np.int64)
+
+    def field(bit):
+        byte, b = bit // 8, bit % 8
+        if byte < 4:
+            return (8 * byte + b, 4)
+        j = byte - 4
+        return (j + (16 if b >= 4 else 0), b % 4)
+
+    _flip_test(decode, 20, field)
+
+
 # ------------------------------------- fp32 dequantizer = exact value rounded
 
-@pytest.mark.parametrize("t", [O.Q4_0, O.Q8_0, O.Q4_K, O.Q6_K, O.Q8_K])
+@pytest.mark.parametrize("t", [O.Q4_0, O.Q8_0, O.Q4_K, O.Q6_K, O.Q8_K, O.Q5_0])
 def test_f32_dequant_is_correctly_rounded_exact_value(t):
     # Each fp32 element has at most one rounding from exact operands, so it
     # must equal the exact (fp64) value rounded once to fp32.  Q4_0, Q8_0 and
@@ -266,7 +306,7 @@ def test_f32_dequant_is_correctly_rounded_exact_value(t):
     S = O.BLOCK_BYTES[t]
     bl = blocks.reshape(rows, nb, S)
     # keep scales finite (NaN/Inf scales are not a parity case)
-    if t in (O.Q4_0, O.Q8_0, O.Q4_K):
+    if t in (O.Q4_0, O.Q8_0, O.Q4_K, O.Q5_0):
         bl[:, :, 1] &= 0x7B
         if t == O.Q4_K:
             bl[:, :, 3] &= 0x7B
@@ -277,7 +317,7 @@ def test_f32_dequant_is_correctly_rounded_exact_value(t):
     f32 = O.dequantize(t, blocks, rows, K)
     f64 = O.dequantize(t, blocks, rows, K, f64=True)
     assert np.array_equal(f32, f64.astype(np.float32))
-    if t in (O.Q4_0, O.Q8_0, O.Q6_K):
+    if t in (O.Q4_0, O.Q8_0, O.Q6_K, O.Q5_0):
         assert np.array_equal(f32.astype(np.float64), f64)
 
 

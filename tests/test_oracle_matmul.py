@@ -50,6 +50,20 @@ def enc_q4_0(q, d_bits=ONE):
     return b.reshape(M, -1)
 
 
+def enc_q5_0(q, d_bits=ONE):
+    """q: (M, K) in 0..31 -> Q5_0 blocks: low parts as Q4_0's nibbles, fifth
+    bit of element e in bit e of the little-endian 32-bit qh."""
+    M, K = q.shape
+    q = q.reshape(M, K // 32, 32).astype(np.int64)
+    b = np.zeros((M, K // 32, 22), np.uint8)
+    b[:, :, 0:2] = h16(d_bits, (M, K // 32))
+    qh = ((q >> 4) << np.arange(32)).sum(axis=2).astype("<u4")
+    b[:, :, 2:6] = qh[..., None].view(np.uint8).reshape(M, K // 32, 4)
+    lo = (q & 15).astype(np.uint8)
+    b[:, :, 6:] = lo[:, :, :16] | (lo[:, :, 16:] << 4)
+    return b.reshape(M, -1)
+
+
 def enc_q4_k_scales(sc, m):
     """sc, m: (..., 8) in 0..63 -> (..., 12) bytes."""
     sc = sc.astype(np.uint8)
@@ -148,6 +162,11 @@ def test_integer_cases_match_int_matmul(seed):
     qn = g.integers(0, 16, (M, K))
     y, _ = O.mul_mat(O.Q4_0, enc_q4_0(qn), enc_q8_0(qx), M, N, K)
     assert np.array_equal(y, (qx @ (qn - 8).T).astype(np.float64))
+    # Q5_0: w = q - 16, q = low nibble | fifth bit << 4
+    q5 = g.integers(0, 32, (M, K))
+    y, _ = O.mul_mat(O.Q5_0, enc_q5_0(q5), enc_q8_0(qx), M, N, K)
+    assert np.array_equal(y, (qx @ (q5 - 16).T).astype(np.float64))
+    assert np.array_equal(O.q5_0_quant_n(enc_q5_0(q5)).reshape(M, K), q5)
     # Q4_K with d = dmin = 1 and random 6-bit scales and mins: w = sc q - m
     K = 256 * int(g.integers(1, 4))
     nb = K // 256
@@ -180,13 +199,15 @@ def _random_case(g, wtype, M, N, K):
         W = synth.q4_k_random(g, M, K)
     elif wtype == O.Q6_K:
         W = synth.q6_k_random(g, M, K)
+    elif wtype == O.Q5_0:
+        W = synth.q5_0_random(g, M, K)
     else:
         W = O.quantize(wtype, synth.normal_f32(g, (M, K), 0.02))
     X = O.quantize(O.VEC_DOT_TYPE[wtype], synth.normal_f32(g, (N, K), 1.0))
     return W, X
 
 
-@pytest.mark.parametrize("wtype", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K])
+@pytest.mark.parametrize("wtype", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K, O.Q5_0])
 def test_blockwise_matches_definition(wtype):
     g = np.random.default_rng(31)
     for M, N, K in ((33, 3, 256), (9, 8, 1024), (1, 1, 256), (64, 17, 512)):
@@ -206,7 +227,7 @@ def test_blockwise_matches_definition(wtype):
         assert np.all(np.abs(y) <= T * (1 + 1e-12))
 
 
-@pytest.mark.parametrize("wtype", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K])
+@pytest.mark.parametrize("wtype", [O.Q8_0, O.Q4_0, O.Q4_K, O.Q6_K, O.Q5_0])
 def test_linear_in_activation_scale(wtype):
     g = np.random.default_rng(37)
     M, N, K = 16, 2, 512
