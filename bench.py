@@ -288,6 +288,58 @@ def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=
             "tops": 2 * M * N * K * launches / sec / 1e12, "copies": copies}
 
 
+def kv_cache_workloads(b: Bench, reps=20):
+    """Q8_0 KV cache of the 8B GQA model (1024 values per token and layer for
+    K and for V): quantizing a 512-token prompt for all 32 layers (one slab),
+    appending one decode token (K and V rows of one layer: a 2-row launch),
+    and reading a 32768-token cache of one layer back to fp32."""
+    import synth
+    torch, Q = b.torch, b.Q
+    row = synth.LLAMA_8B_KV_ROW
+    rowb = Q.qmm_row_bytes(Q.QMM_Q8_0, row)
+    g = synth.rng(0)
+    out = {}
+    # prefill: 2 x 32 layers x 512 tokens = 32768 rows
+    rows = 2 * synth.LLAMA_8B_KV["layers"] * 512
+    x = torch.from_numpy(synth.normal_f32(g, (rows, row), 1.0)).to(b.dev)
+    cache = torch.empty((rows, rowb), dtype=torch.uint8, device=b.dev)
+    lib = Q.lib()
+
+    def quant():
+        lib.qmm_quantize_act(Q.QMM_Q8_0, x.data_ptr(), cache.data_ptr(), rows, row,
+                             torch.cuda.current_stream().cuda_stream)
+    sec = b.time_graph(b.graph(quant), reps, 2)
+    by = rows * row * 4 + rows * rowb
+    out["kv_q8_0_prefill_quantize_32768x1024"] = {"us_per_launch": sec / reps * 1e6, "bytes_per_launch": by,
+                                                  "gbs": by * reps / sec / 1e9}
+    # decode append: one token's K and V rows for each of the 32 layers, one
+    # 2-row launch per layer (32 launches in the graph)
+    L = synth.LLAMA_8B_KV["layers"]
+
+    def append():
+        st = torch.cuda.current_stream().cuda_stream
+        for layer in range(L):
+            lib.qmm_quantize_act(Q.QMM_Q8_0, x.data_ptr() + 2 * layer * row * 4,
+                                 cache.data_ptr() + (2 * layer * 512 + 7) * rowb, 2, row, st)
+    sec = b.time_graph(b.graph(append), reps, 2)
+    by = 2 * (row * 4 + rowb)
+    out["kv_q8_0_decode_append_2x1024"] = {"us_per_launch": sec / (reps * L) * 1e6, "bytes_per_launch": by,
+                                           "launches_per_token": L}
+    # read back one layer's 32768-token K cache
+    deq = torch.empty((rows, row), dtype=torch.float32, device=b.dev)
+
+    def dequant():
+        lib.qmm_dequantize(Q.QMM_Q8_0, cache.data_ptr(), deq.data_ptr(), rows, row,
+                           torch.cuda.current_stream().cuda_stream)
+    sec = b.time_graph(b.graph(dequant), reps, 2)
+    by = rows * rowb + rows * row * 4
+    out["kv_q8_0_dequantize_32768x1024"] = {"us_per_launch": sec / reps * 1e6, "bytes_per_launch": by,
+                                            "gbs": by * reps / sec / 1e9}
+    del x, cache, deq
+    torch.cuda.empty_cache()
+    return out
+
+
 def secondary(b: Bench):
     import oracle as O
     import synth
@@ -309,6 +361,8 @@ def secondary(b: Bench):
         r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
         out[f"q4_k_gemm_{M}x4096_b512"] = r
         progress(f"q4_k gemm {M}x4096 b512 {r['tops']:.1f} TOPS")
+    out.update(kv_cache_workloads(b))
+    progress("kv cache q8_0 done")
     return out
 
 

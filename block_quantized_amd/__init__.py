@@ -18,11 +18,12 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqmm.so")
 
-QMM_Q4_0, QMM_Q8_0, QMM_Q4_K, QMM_Q6_K, QMM_Q8_K = 1, 2, 3, 4, 5
+QMM_Q4_0, QMM_Q8_0, QMM_Q4_K, QMM_Q6_K, QMM_Q8_K, QMM_Q5_0 = 1, 2, 3, 4, 5, 6
 QMM_OK, QMM_ERR_TYPE, QMM_ERR_SHAPE, QMM_ERR_NULL = 0, -1, -2, -3
 QMM_ERR_ALIGN, QMM_ERR_UNSUPPORTED, QMM_ERR_HIP = -4, -5, -6
 
-TYPES = {"Q4_0": QMM_Q4_0, "Q8_0": QMM_Q8_0, "Q4_K": QMM_Q4_K, "Q6_K": QMM_Q6_K, "Q8_K": QMM_Q8_K}
+TYPES = {"Q4_0": QMM_Q4_0, "Q8_0": QMM_Q8_0, "Q4_K": QMM_Q4_K, "Q6_K": QMM_Q6_K, "Q8_K": QMM_Q8_K,
+         "Q5_0": QMM_Q5_0}
 
 _lib = None
 

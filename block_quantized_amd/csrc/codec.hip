@@ -150,6 +150,27 @@ __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* __rest
     reinterpret_cast<float4*>(out)[t] = r;
 }
 
+// Q5_0: as Q4_0's nibbles, plus the fifth bit of element e from bit e of
+// the little-endian 32-bit qh; w = d (q - 16), exact in fp32.
+__global__ __launch_bounds__(256) void dequant_q5_0_kernel(const uint8_t* __restrict__ w, float* __restrict__ out,
+                                                           int64_t nquads) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= nquads) return;
+    const int64_t b = t >> 3;
+    const int sub = (int)(t & 7);
+    const uint8_t* blk = w + b * kQ5_0Bytes;
+    const float d = h2f(reinterpret_cast<const uint16_t*>(blk)[0]);
+    const uint32_t qh = ld_u16x2(blk + 2) >> (4 * sub);  // bits of elements 4 sub .. 4 sub + 3
+    uint32_t qs = ld_u16x2(blk + 6 + 4 * (sub & 3));
+    if (sub >= 4) qs >>= 4;
+    float4 r;
+    r.x = d * (float)((int)((qs & 15) | ((qh & 1) << 4)) - 16);
+    r.y = d * (float)((int)(((qs >> 8) & 15) | (((qh >> 1) & 1) << 4)) - 16);
+    r.z = d * (float)((int)(((qs >> 16) & 15) | (((qh >> 2) & 1) << 4)) - 16);
+    r.w = d * (float)((int)(((qs >> 24) & 15) | (((qh >> 3) & 1) << 4)) - 16);
+    reinterpret_cast<float4*>(out)[t] = r;
+}
+
 __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t* __restrict__ w, float* __restrict__ out,
                                                            int64_t nquads) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -271,6 +292,7 @@ hipError_t launch_dequantize(int t, const void* blocks, float* out, int64_t rows
     switch (t) {
     case QMM_Q4_0: hipLaunchKernelGGL(dequant_q4_0_kernel, g, blk, 0, s, w, out, nq); break;
     case QMM_Q8_0: hipLaunchKernelGGL(dequant_q8_0_kernel, g, blk, 0, s, w, out, nq); break;
+    case QMM_Q5_0: hipLaunchKernelGGL(dequant_q5_0_kernel, g, blk, 0, s, w, out, nq); break;
     case QMM_Q4_K: hipLaunchKernelGGL(dequant_q4_k_kernel, g, blk, 0, s, w, out, nq); break;
     case QMM_Q6_K: hipLaunchKernelGGL(dequant_q6_k_kernel, g, blk, 0, s, w, out, nq); break;
     case QMM_Q8_K: hipLaunchKernelGGL(dequant_q8_k_kernel, g, blk, 0, s, w, out, nq); break;

@@ -43,6 +43,7 @@ namespace {
 template <int WT> struct U;
 template <> struct U<QMM_Q4_0> { static constexpr int UB = 144, NV = 9, SUB = 1, WPU = 256; };
 template <> struct U<QMM_Q8_0> { static constexpr int UB = 272, NV = 17, SUB = 1, WPU = 256; };
+template <> struct U<QMM_Q5_0> { static constexpr int UB = 176, NV = 11, SUB = 1, WPU = 256; };
 template <> struct U<QMM_Q4_K> { static constexpr int UB = 144, NV = 9, SUB = 1, WPU = 256; };
 template <> struct U<QMM_Q6_K> { static constexpr int UB = 8 * kQ6_KBytes, NV = 14, SUB = 8, WPU = 2048; };
 
@@ -97,7 +98,7 @@ struct RoundTag {
 
 template <int WT, int NC, bool XF, class Hook>
 __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, Hook&& after_loads) {
-    constexpr bool kQ80 = (WT == QMM_Q4_0 || WT == QMM_Q8_0);
+    constexpr bool kQ80 = (WT == QMM_Q4_0 || WT == QMM_Q5_0 || WT == QMM_Q8_0);
     constexpr int KB = XF ? 1 : 4;  // items per thread per round
     const int nitems = kQ80 ? NC * G * 8 : NC * G * 4;
     const int step = KB * blockDim.x;
@@ -379,6 +380,57 @@ __device__ __forceinline__ void unit_q4_0(const uint32_t* w, const uint8_t* xr0,
     }
 }
 
+// Fifth bits b3..b0 (of four consecutive elements) to bit 4 of four bytes:
+// v * 0x00204081 places bit k at bit 8k (the four shifted copies do not
+// overlap, so there are no carries).
+__device__ __forceinline__ uint32_t fifth_bits(uint32_t v4) {
+    return ((v4 * 0x00204081u) & 0x01010101u) << 4;
+}
+
+// Q5_0: eight 22-byte blocks per 176-byte unit; block i starts at byte 22i,
+// i.e. dword 11i/2 for even i and two bytes into dword (22i-2)/4 for odd i.
+template <int NC>
+__device__ __forceinline__ void unit_q5_0(const uint32_t* w, const uint8_t* xr0, int xstride, float (&acc)[NC]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t db, qh, q[4];
+        if ((i & 1) == 0) {
+            const int b = 11 * i / 2;
+            db = w[b];
+            qh = __builtin_amdgcn_alignbyte(w[b + 1], w[b], 2);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_alignbyte(w[b + 2 + k], w[b + 1 + k], 2);
+        } else {
+            const int b = (22 * i - 2) / 4;
+            db = w[b] >> 16;
+            qh = w[b + 1];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[k] = w[b + 2 + k];
+        }
+        const float dw = h2f(db);
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            lo[k] = (q[k] & 0x0F0F0F0Fu) | fifth_bits((qh >> (4 * k)) & 15u);
+            hi[k] = ((q[k] >> 4) & 0x0F0F0F0Fu) | fifth_bits((qh >> (16 + 4 * k)) & 15u);
+        }
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const uint32_t* xr = reinterpret_cast<const uint32_t*>(xr0 + n * xstride);
+            int dot = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                dot = dot4(lo[k], xr[8 * i + k], dot);
+                dot = dot4(hi[k], xr[8 * i + 4 + k], dot);
+            }
+            // the record holds 8 * sum q_x (Q4_0's offset); Q5_0's is 16 * sum q_x
+            const int isum = dot - 2 * reinterpret_cast<const int*>(xr)[72 + i];
+            const float dx = reinterpret_cast<const float*>(xr)[64 + i];
+            acc[n] += (float)isum * (dw * dx);
+        }
+    }
+}
+
 template <int NC>
 __device__ __forceinline__ void unit_q8_0(const uint32_t* w, const uint8_t* xr0, int xstride, float (&acc)[NC]) {
 #pragma unroll
@@ -606,6 +658,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
             const uint32_t* w = reinterpret_cast<const uint32_t*>(buf[B]);
             const uint8_t* xr0 = xl + (cur.g + J) * XREC;
             if constexpr (WT == QMM_Q4_0) unit_q4_0<NC>(w, xr0, xstride, acc);
+            else if constexpr (WT == QMM_Q5_0) unit_q5_0<NC>(w, xr0, xstride, acc);
             else if constexpr (WT == QMM_Q8_0) unit_q8_0<NC>(w, xr0, xstride, acc);
             else if constexpr (WT == QMM_Q4_K) unit_q4_k<NC>(w, xr0, xstride, acc);
             else unit_q6_k<NC, 2 * J>(w, xr0, xstride, acc);  // super-block J starts 2J bytes into its window
@@ -687,8 +740,8 @@ __global__ __launch_bounds__(256) void gemv_rowwave_kernel(const uint8_t* __rest
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= M) return;
-    if constexpr (WT == QMM_Q4_0 || WT == QMM_Q8_0) {
-        constexpr int WB = (WT == QMM_Q4_0) ? kQ4_0Bytes : kQ8_0Bytes;
+    if constexpr (WT == QMM_Q4_0 || WT == QMM_Q5_0 || WT == QMM_Q8_0) {
+        constexpr int WB = (WT == QMM_Q4_0) ? kQ4_0Bytes : (WT == QMM_Q5_0) ? kQ5_0Bytes : kQ8_0Bytes;
         const int64_t nb = K / 32;
         for (int n = 0; n < N; ++n) {
             float acc = 0.f;
@@ -710,6 +763,19 @@ __global__ __launch_bounds__(256) void gemv_rowwave_kernel(const uint8_t* __rest
                         sx = dot4(x1, 0x01010101u, sx);
                     }
                     dot -= 8 * sx;
+                } else if constexpr (WT == QMM_Q5_0) {
+                    const uint32_t qh = ld_u16x2_g(wb + 2);
+                    int sx = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t q = ld_u16x2_g(wb + 6 + 4 * k);
+                        const uint32_t x0 = ld_u16x2_g(xb + 2 + 4 * k), x1 = ld_u16x2_g(xb + 18 + 4 * k);
+                        dot = dot4((q & 0x0F0F0F0Fu) | fifth_bits((qh >> (4 * k)) & 15u), x0, dot);
+                        dot = dot4(((q >> 4) & 0x0F0F0F0Fu) | fifth_bits((qh >> (16 + 4 * k)) & 15u), x1, dot);
+                        sx = dot4(x0, 0x01010101u, sx);
+                        sx = dot4(x1, 0x01010101u, sx);
+                    }
+                    dot -= 16 * sx;
                 } else {
 #pragma unroll
                     for (int k = 0; k < 8; ++k)
@@ -839,7 +905,8 @@ hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const i
     }
     for (int i = nseg; i < kMaxSeg; ++i) a.seg[i] = a.seg[0];
     a.nwork = work;
-    const int64_t xrowB = xf32 ? K * 4 : (int64_t)a.G * (WT == QMM_Q4_0 || WT == QMM_Q8_0 ? 8 * kQ8_0Bytes : kQ8_KBytes);
+    const int64_t xrowB =
+        xf32 ? K * 4 : (int64_t)a.G * (WT == QMM_Q4_0 || WT == QMM_Q5_0 || WT == QMM_Q8_0 ? 8 * kQ8_0Bytes : kQ8_KBytes);
     // waves per workgroup: spread small problems over all CUs.  A launch that
     // quantizes x itself uses 2 to 4 waves: enough lanes to share each
     // block's quantization, few enough that one compute unit's W requests do
@@ -869,6 +936,7 @@ hipError_t rowwave(int wtype, const void* W, const void* xq, float* y, int64_t M
     const uint8_t* x = static_cast<const uint8_t*>(xq);
     if (wtype == QMM_Q4_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q4_0>, g, b, 0, s, w, x, y, M, (int)N, K);
     else if (wtype == QMM_Q8_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q8_0>, g, b, 0, s, w, x, y, M, (int)N, K);
+    else if (wtype == QMM_Q5_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q5_0>, g, b, 0, s, w, x, y, M, (int)N, K);
     else if (wtype == QMM_Q6_K) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q6_K>, g, b, 0, s, w, x, y, M, (int)N, K);
     else return hipErrorInvalidValue;
     return hipGetLastError();
@@ -897,6 +965,7 @@ hipError_t launch_gemv_multi(int wtype, int count, const void* const* W, float* 
     switch (wtype) {
     case QMM_Q4_0: return gemv_typed<QMM_Q4_0>(count, W, y, M, x, x_f32, N, K, s);
     case QMM_Q8_0: return gemv_typed<QMM_Q8_0>(count, W, y, M, x, x_f32, N, K, s);
+    case QMM_Q5_0: return gemv_typed<QMM_Q5_0>(count, W, y, M, x, x_f32, N, K, s);
     case QMM_Q4_K: return gemv_typed<QMM_Q4_K>(count, W, y, M, x, x_f32, N, K, s);
     case QMM_Q6_K: return gemv_typed<QMM_Q6_K>(count, W, y, M, x, x_f32, N, K, s);
     default: return hipErrorInvalidValue;

@@ -12,8 +12,10 @@ namespace {
 
 constexpr int64_t kMaxK = 65536;  // activation rows must fit the GEMV's LDS staging
 
-bool is_type(int t) { return t >= QMM_Q4_0 && t <= QMM_Q8_K; }
-bool is_weight(int t) { return t == QMM_Q4_0 || t == QMM_Q8_0 || t == QMM_Q4_K || t == QMM_Q6_K; }
+bool is_type(int t) { return t >= QMM_Q4_0 && t <= QMM_Q5_0; }
+bool is_weight(int t) {
+    return t == QMM_Q4_0 || t == QMM_Q5_0 || t == QMM_Q8_0 || t == QMM_Q4_K || t == QMM_Q6_K;
+}
 
 int check_ptr(const void* p) {
     if (!p) return QMM_ERR_NULL;
@@ -50,7 +52,7 @@ size_t qmm_row_bytes(int type, int64_t K) {
 
 int qmm_vec_dot_type(int wtype) {
     if (!is_type(wtype)) return QMM_ERR_TYPE;
-    if (wtype == QMM_Q4_0 || wtype == QMM_Q8_0) return QMM_Q8_0;
+    if (wtype == QMM_Q4_0 || wtype == QMM_Q5_0 || wtype == QMM_Q8_0) return QMM_Q8_0;
     if (wtype == QMM_Q4_K || wtype == QMM_Q6_K) return QMM_Q8_K;
     return QMM_ERR_UNSUPPORTED;
 }

@@ -13,13 +13,15 @@ namespace qmm {
 
 // Block geometry of the format table (page "The GGML ecosystem, and where
 // synapse fits", §5 "Quantization").
-constexpr int kQ4_0Bytes = 18, kQ8_0Bytes = 34, kQ4_KBytes = 144, kQ6_KBytes = 210, kQ8_KBytes = 292;
+constexpr int kQ4_0Bytes = 18, kQ8_0Bytes = 34, kQ4_KBytes = 144, kQ6_KBytes = 210, kQ8_KBytes = 292,
+              kQ5_0Bytes = 22;
 
 __host__ __device__ constexpr int block_size(int t) {
-    return (t == QMM_Q4_0 || t == QMM_Q8_0) ? 32 : (t == QMM_Q4_K || t == QMM_Q6_K || t == QMM_Q8_K) ? 256 : 0;
+    return (t == QMM_Q4_0 || t == QMM_Q8_0 || t == QMM_Q5_0) ? 32
+         : (t == QMM_Q4_K || t == QMM_Q6_K || t == QMM_Q8_K) ? 256 : 0;
 }
 __host__ __device__ constexpr int block_bytes(int t) {
-    return t == QMM_Q4_0 ? kQ4_0Bytes : t == QMM_Q8_0 ? kQ8_0Bytes : t == QMM_Q4_K ? kQ4_KBytes
+    return t == QMM_Q4_0 ? kQ4_0Bytes : t == QMM_Q5_0 ? kQ5_0Bytes : t == QMM_Q8_0 ? kQ8_0Bytes : t == QMM_Q4_K ? kQ4_KBytes
          : t == QMM_Q6_K ? kQ6_KBytes : t == QMM_Q8_K ? kQ8_KBytes : 0;
 }
 

@@ -60,17 +60,23 @@ extern "C" {
  *                   gives no Q6_K formula)
  *   Q8_K 256 / 292  fp32 d; 256 int8 quants; 16 int16 sums of 16 quants;
  *                   activations only
+ *   Q5_0  32 / 22   fp16 d; a 32-bit word of fifth bits; 32 four-bit low
+ *                   parts; w = d (q - 16).  The type for rows whose length
+ *                   is not a multiple of 256 (§3, fallback rule).
  * Bit arrangement inside a block: GGUF's on-disk arrangement (the pages give
  * field lists only): Q4_0 [d][qs:16] with element e<16 in the low nibble of
  * qs[e] and e>=16 in the high nibble of qs[e-16]; Q8_0 [d][qs:32];
  * Q4_K [d][dmin][scales:12][qs:128]; Q6_K [ql:128][qh:64][scales:16][d];
- * Q8_K [d:f32][qs:256][bsums:16 x int16]. */
+ * Q8_K [d:f32][qs:256][bsums:16 x int16]; Q5_0 [d][qh:4][qs:16] with the
+ * low four bits arranged as Q4_0's nibbles and the fifth bit of element e in
+ * bit e of the little-endian qh (this library's reading). */
 typedef enum {
     QMM_Q4_0 = 1,
     QMM_Q8_0 = 2,
     QMM_Q4_K = 3,
     QMM_Q6_K = 4,
-    QMM_Q8_K = 5
+    QMM_Q8_K = 5,
+    QMM_Q5_0 = 6
 } qmm_type;
 
 /* Status codes. */
@@ -86,13 +92,13 @@ enum {
 
 /* Values per block (32 or 256); 0 for an unknown type. */
 int qmm_block_size(int type);
-/* Bytes per block (18, 34, 144, 210, 292); 0 for an unknown type. */
+/* Bytes per block (18, 34, 144, 210, 292, 22); 0 for an unknown type. */
 size_t qmm_block_bytes(int type);
 /* Bytes of one row of K values; 0 if the type is unknown, K <= 0 or K is not
  * a multiple of the block size. */
 size_t qmm_row_bytes(int type, int64_t K);
 /* The activation type a weight type is dotted with (page "The GGML
- * ecosystem...", §5, vec_dot_type): Q4_0, Q8_0 -> Q8_0; Q4_K, Q6_K -> Q8_K.
+ * ecosystem...", §5, vec_dot_type): Q4_0, Q5_0, Q8_0 -> Q8_0; Q4_K, Q6_K -> Q8_K.
  * Returns QMM_ERR_TYPE or QMM_ERR_UNSUPPORTED (Q8_K is never a weight). */
 int qmm_vec_dot_type(int wtype);
 
@@ -121,13 +127,13 @@ int qmm_quantize(int dst, const float* x, void* out, int64_t rows, int64_t K, vo
  * lookups and norm weights).  All five types.
  *   blocks : device, rows x qmm_row_bytes(type, K) bytes
  *   out    : device, rows x K fp32, written
- * Element values, computed in fp32 in this order: Q4_0 d*(q-8); Q8_0 d*q;
+ * Element values, computed in fp32 in this order: Q4_0 d*(q-8); Q5_0 d*(q-16); Q8_0 d*q;
  * Q4_K (d*sc)*q - (dmin*m); Q6_K (d*sc)*(q-32); Q8_K d*q.  Every product is
  * exact in fp32 except Q8_K's, so results are the exact value rounded once. */
 int qmm_dequantize(int type, const void* blocks, float* out, int64_t rows, int64_t K, void* stream);
 
 /* y = W x^T over quantized weights and pre-quantized activations.
- *   wtype : QMM_Q4_0, QMM_Q8_0, QMM_Q4_K or QMM_Q6_K
+ *   wtype : QMM_Q4_0, QMM_Q5_0, QMM_Q8_0, QMM_Q4_K or QMM_Q6_K
  *   W     : device, M x qmm_row_bytes(wtype, K) bytes of raw blocks
  *   xq    : device, N x qmm_row_bytes(qmm_vec_dot_type(wtype), K) bytes
  *   y     : device, N x M fp32, written (y[n*M + m])

@@ -42,6 +42,9 @@ def test_sizes(L):
     assert Q.qmm_vec_dot_type(Q.QMM_Q8_0) == Q.QMM_Q8_0
     assert Q.qmm_vec_dot_type(Q.QMM_Q4_K) == Q.QMM_Q8_K
     assert Q.qmm_vec_dot_type(Q.QMM_Q6_K) == Q.QMM_Q8_K
+    assert Q.qmm_vec_dot_type(Q.QMM_Q5_0) == Q.QMM_Q8_0
+    assert Q.qmm_block_size(Q.QMM_Q5_0) == 32 and Q.qmm_block_bytes(Q.QMM_Q5_0) == 22
+    assert Q.qmm_row_bytes(Q.QMM_Q5_0, 896) == 28 * 22 and Q.qmm_block_size(7) == 0
     assert Q.qmm_vec_dot_type(Q.QMM_Q8_K) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_vec_dot_type(42) == Q.QMM_ERR_TYPE
     for c in (0, -1, -2, -3, -4, -5, -6, -99):
@@ -58,6 +61,8 @@ def test_quantize_errors(L):
     assert Q.qmm_quantize_act(Q.QMM_Q4_0, A, A, 1, 32, S) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_quantize_act(Q.QMM_Q4_K, A, A, 1, 256, S) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_quantize(Q.QMM_Q6_K, A, A, 1, 256, S) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_quantize(Q.QMM_Q5_0, A, A, 1, 256, S) == Q.QMM_ERR_UNSUPPORTED
+    assert Q.qmm_quantize_act(Q.QMM_Q5_0, A, A, 1, 256, S) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_quantize_act(Q.QMM_Q8_0, 0, A, 1, 32, S) == Q.QMM_ERR_NULL
     assert Q.qmm_quantize_act(Q.QMM_Q8_0, A, 0, 1, 32, S) == Q.QMM_ERR_NULL
     assert Q.qmm_quantize_act(Q.QMM_Q8_0, A + 4, A, 1, 32, S) == Q.QMM_ERR_ALIGN
@@ -87,6 +92,8 @@ def test_mul_mat_errors(L):
     assert mm(Q.QMM_Q4_K, A, A, A + 4, 4, 1, 256, S) == Q.QMM_ERR_ALIGN
     assert mm(Q.QMM_Q4_K, A, A, A, 4, 1, 128, S) == Q.QMM_ERR_SHAPE   # K % 256
     assert mm(Q.QMM_Q4_0, A, A, A, 4, 1, 48, S) == Q.QMM_ERR_SHAPE    # K % 32
+    assert mm(Q.QMM_Q5_0, A, A, A, 4, 1, 48, S) == Q.QMM_ERR_SHAPE
+    assert mm(7, A, A, A, 4, 1, 32, S) == Q.QMM_ERR_TYPE
     assert mm(Q.QMM_Q4_0, A, A, A, 0, 1, 32, S) == Q.QMM_ERR_SHAPE
     assert mm(Q.QMM_Q4_0, A, A, A, 4, 0, 32, S) == Q.QMM_ERR_SHAPE
     assert mm(Q.QMM_Q4_0, A, A, A, 2 ** 31, 1, 32, S) == Q.QMM_ERR_SHAPE
