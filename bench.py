@@ -361,6 +361,13 @@ def secondary(b: Bench):
         r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
         out[f"q4_k_gemm_{M}x4096_b512"] = r
         progress(f"q4_k gemm {M}x4096 b512 {r['tops']:.1f} TOPS")
+    for name, wt, mk in (("q4_0", b.Q.QMM_Q4_0, lambda g, M, K: O.quantize(O.Q4_0, synth.normal_f32(g, (M, K), 0.02))),
+                         ("q5_0", b.Q.QMM_Q5_0, synth.q5_0_random),
+                         ("q8_0", b.Q.QMM_Q8_0, lambda g, M, K: O.quantize(O.Q8_0, synth.normal_f32(g, (M, K), 0.02)))):
+        r = gemv_workload(b, wt, 4096, 4096, 512, mk, min_bytes=1, reps_floor=5)
+        r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
+        out[f"{name}_gemm_4096x4096_b512"] = r
+        progress(f"{name} gemm 4096x4096 b512 {r['tops']:.1f} TOPS")
     out.update(kv_cache_workloads(b))
     progress("kv cache q8_0 done")
     return out

@@ -45,7 +45,9 @@ namespace qmm {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-// 8 and 16 bytes at a 2-byte-aligned address (Q6_K super-blocks are 210 bytes)
+// 4, 8 and 16 bytes at a 2-byte-aligned address (Q6_K super-blocks are 210
+// bytes, Q5_0 and Q8_0 blocks 22 and 34)
+typedef uint32_t u32_a2 __attribute__((aligned(2)));
 typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 // 8 and 16 bytes at a 4-byte-aligned address (Q8_K blocks are 292 bytes)
@@ -430,9 +432,179 @@ __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict
     }
 }
 
+// ------------------------------------------------- Q4_0, Q5_0, Q8_0 weights
+// 32-value blocks with one fp16 scale each, against Q8_0 activations.  The
+// weight codes enter the MFMA as int8 (q - 8, q - 16 or q itself), one
+// v_mfma_i32_32x32x32_i8 per block and activation tile, and each block's
+// integer tile is scaled by d_w * d_x in fp32 (the scales change every 32
+// values, so this epilogue, not the matrix core, bounds the kernel).
+// K runs in chunks of 4 blocks; the activation chunk of 64 rows is staged in
+// LDS (codes at row stride 144, scales as [block][row] floats).
+template <int WT>
+struct Q32W;  // per-lane weight operand of one block: row c, values 16h .. 16h+15
+template <>
+struct Q32W<QMM_Q8_0> {
+    static constexpr int kBytes = kQ8_0Bytes;
+    uint32_t d;
+    u32x4_a2 q;
+    __device__ void load(const uint8_t* b, int h) {
+        d = *reinterpret_cast<const uint16_t*>(b);
+        q = *reinterpret_cast<const u32x4_a2*>(b + 2 + 16 * h);
+    }
+    __device__ v4i operand(int) const { return (v4i){(int)q.x, (int)q.y, (int)q.z, (int)q.w}; }
+};
+// 4-bit codes (0..15) minus 8 as int8: (t ^ 8) is the 4-bit two's complement,
+// and bit 3 copied to bits 4-7 sign-extends it (0x08 * 0x1E = 0xF0, no carry)
+__device__ __forceinline__ uint32_t nibbles_minus_8(uint32_t t) {
+    t ^= 0x08080808u;
+    return t | ((t & 0x08080808u) * 0x1Eu);
+}
+template <>
+struct Q32W<QMM_Q4_0> {
+    static constexpr int kBytes = kQ4_0Bytes;
+    uint32_t d;
+    u32x4_a2 q;
+    __device__ void load(const uint8_t* b, int) {
+        d = *reinterpret_cast<const uint16_t*>(b);
+        q = *reinterpret_cast<const u32x4_a2*>(b + 2);
+    }
+    __device__ v4i operand(int h) const {  // values 0-15: low nibbles, 16-31: high
+        const int sh = 4 * h;
+        return (v4i){(int)nibbles_minus_8((q.x >> sh) & 0x0F0F0F0Fu), (int)nibbles_minus_8((q.y >> sh) & 0x0F0F0F0Fu),
+                     (int)nibbles_minus_8((q.z >> sh) & 0x0F0F0F0Fu), (int)nibbles_minus_8((q.w >> sh) & 0x0F0F0F0Fu)};
+    }
+};
+// 5-bit codes minus 16: bits 0-3 from the nibble, bit 4 from qh; as for Q4_0,
+// (q ^ 16) is the 5-bit two's complement, sign-extended from bit 4
+__device__ __forceinline__ uint32_t q5_minus_16(uint32_t nib, uint32_t bits4) {
+    uint32_t t = nib | (((bits4 * 0x00204081u) & 0x01010101u) << 4);
+    t ^= 0x10101010u;
+    return t | ((t & 0x10101010u) * 0x0Eu);
+}
+template <>
+struct Q32W<QMM_Q5_0> {
+    static constexpr int kBytes = kQ5_0Bytes;
+    uint32_t d, qh;
+    u32x4_a2 q;
+    __device__ void load(const uint8_t* b, int) {
+        d = *reinterpret_cast<const uint16_t*>(b);
+        qh = *reinterpret_cast<const u32_a2*>(b + 2);
+        q = *reinterpret_cast<const u32x4_a2*>(b + 6);
+    }
+    __device__ v4i operand(int h) const {
+        const int sh = 4 * h;
+        const uint32_t hb = qh >> (16 * h);
+        return (v4i){(int)q5_minus_16((q.x >> sh) & 0x0F0F0F0Fu, hb & 15u),
+                     (int)q5_minus_16((q.y >> sh) & 0x0F0F0F0Fu, (hb >> 4) & 15u),
+                     (int)q5_minus_16((q.z >> sh) & 0x0F0F0F0Fu, (hb >> 8) & 15u),
+                     (int)q5_minus_16((q.w >> sh) & 0x0F0F0F0Fu, (hb >> 12) & 15u)};
+    }
+};
+
+template <int WT>
+__global__ __launch_bounds__(256, 2) void gemm_q32_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
+                                                       float* __restrict__ Y, int M, int N, int NB,
+                                                       int mblk, int nblk) {
+    constexpr int BN = 64, CB = 4;          // activation rows per workgroup, blocks per chunk
+    constexpr int CS = 32 * CB + 16;        // LDS row stride of a chunk's codes
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][CS];
+    __shared__ __attribute__((aligned(16))) float s_dx[2][CB][BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 31, h = lane >> 5;
+    int rb, cb;
+    if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
+    const int m0 = rb * 128 + wave * 32;
+    const int n0 = cb * BN;
+    const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
+    const uint8_t* wrow = W + (int64_t)mrow * NB * Q32W<WT>::kBytes;
+    const int nch = NB / CB, tail = NB % CB;  // full chunks; blocks in the last, partial one
+
+    // activation staging: thread = (row rn, block jb) of the chunk
+    const int rn = tid >> 2, jb = tid & 3;
+    const uint8_t* xrow = X + (int64_t)min(n0 + rn, N - 1) * NB * kQ8_0Bytes;
+    u32x4_a2 xq0, xq1;
+    uint32_t xdb;
+    auto x_load = [&](int ch) {
+        const int blk = min(ch * CB + jb, NB - 1);  // a partial chunk repeats its last block
+        const uint8_t* p = xrow + (int64_t)blk * kQ8_0Bytes;
+        xdb = *reinterpret_cast<const uint16_t*>(p);
+        xq0 = *reinterpret_cast<const u32x4_a2*>(p + 2);
+        xq1 = *reinterpret_cast<const u32x4_a2*>(p + 18);
+    };
+    auto x_store = [&](int buf) {
+        uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][32 * jb]);
+        dst[0] = make_uint4(xq0.x, xq0.y, xq0.z, xq0.w);
+        dst[1] = make_uint4(xq1.x, xq1.y, xq1.z, xq1.w);
+        s_dx[buf][jb][rn] = h2f(xdb);
+    };
+    Q32W<WT> wn[CB];
+    auto w_load = [&](int ch) {
+#pragma unroll
+        for (int j = 0; j < CB; ++j) wn[j].load(wrow + (int64_t)min(ch * CB + j, NB - 1) * Q32W<WT>::kBytes, h);
+    };
+
+    float yacc[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
+
+    const int nchunks = nch + (tail ? 1 : 0);
+    x_load(0);
+    w_load(0);
+    x_store(0);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int buf = ch & 1;
+        Q32W<WT> w[CB];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) w[j] = wn[j];
+        if (ch + 1 < nchunks) {
+            x_load(ch + 1);
+            w_load(ch + 1);
+        }
+        const int nb = (ch < nch) ? CB : tail;  // blocks in this chunk
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            if (j < nb) {
+                const v4i bq = w[j].operand(h);
+                const float dw = h2f(w[j].d);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const v4i a = *reinterpret_cast<const v4i*>(&s_codes[buf][32 * t + c][32 * j + 16 * h]);
+                    const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, (v16i){}, 0, 0, 0);
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const float4 dx = *reinterpret_cast<const float4*>(&s_dx[buf][j][32 * t + 8 * qd + 4 * h]);
+                        const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) yacc[t][4 * qd + e] += (dw * dxa[e]) * (float)p[4 * qd + e];
+                    }
+                }
+            }
+        }
+        if (ch + 1 < nchunks) x_store(buf ^ 1);
+        __syncthreads();
+    }
+
+    const int m = m0 + c;
+    if (m < M) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = n0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (n < N) Y[(int64_t)n * M + m] = yacc[t][r];
+            }
+    }
+}
+
 }  // namespace
 
-bool gemm_supported(int wtype) { return wtype == QMM_Q4_K || wtype == QMM_Q6_K; }
+bool gemm_supported(int wtype) {
+    return wtype == QMM_Q4_K || wtype == QMM_Q6_K || wtype == QMM_Q4_0 || wtype == QMM_Q5_0 || wtype == QMM_Q8_0;
+}
 
 hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
@@ -446,6 +618,18 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
     const int64_t tiles_max = (int64_t)mblocks * ((N + 63) / 64);
     if (8 * ((tiles_max + 7) / 8) * 256 > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
     auto grid = [](int64_t tiles) { return dim3((unsigned)(8 * ((tiles + 7) / 8))); };
+    if (wtype == QMM_Q4_0 || wtype == QMM_Q5_0 || wtype == QMM_Q8_0) {
+        const int64_t nb = (N + 63) / 64;
+        const int NB = (int)(K / 32);
+        const dim3 g = grid(mblocks * nb);
+        if (wtype == QMM_Q4_0)
+            hipLaunchKernelGGL(gemm_q32_kernel<QMM_Q4_0>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+        else if (wtype == QMM_Q5_0)
+            hipLaunchKernelGGL(gemm_q32_kernel<QMM_Q5_0>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+        else
+            hipLaunchKernelGGL(gemm_q32_kernel<QMM_Q8_0>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+        return hipGetLastError();
+    }
     if (wtype == QMM_Q6_K) {
         // bound by streaming W: one 32-row activation tile per workgroup up to
         // N = 32 (W read once), wider tiles beyond

@@ -100,7 +100,7 @@ def test_mul_mat_errors(L):
     assert mm(Q.QMM_Q6_K, A, A, A, 4, 1, 65536 + 256, S) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_mul_mat_algo(Q.QMM_Q4_0, A, A, A, 4, 1, 32, 3, S) == Q.QMM_ERR_UNSUPPORTED
     assert Q.qmm_mul_mat_algo(Q.QMM_Q4_0, A, A, A, 4, 1, 32, -1, S) == Q.QMM_ERR_UNSUPPORTED
-    assert Q.qmm_mul_mat_algo(Q.QMM_Q4_0, A, A, A, 4, 16, 32, 2, S) == Q.QMM_ERR_UNSUPPORTED  # no Q4_0 GEMM yet
+    assert Q.qmm_mul_mat_algo(Q.QMM_Q8_K, A, A, A, 4, 16, 256, 2, S) == Q.QMM_ERR_UNSUPPORTED  # Q8_K is never a weight
 
 
 def test_binding_has_no_fallback(monkeypatch, tmp_path):

@@ -152,3 +152,55 @@ def test_gemm_q6k_deterministic_in_bounds_and_matches_gemv():
     y_gemv = to_cpu(Q.mul_mat(Q.QMM_Q6_K, W, xq, M, N, K, algo=1)).reshape(-1)
     y_ref, T = O.mul_mat(O.Q6_K, to_cpu(W), to_cpu(xq), M, N, K)
     assert np.all(np.abs(outs[0].astype(np.float64) - y_gemv) <= 2e-5 * T.reshape(-1))
+
+
+# ----------------------------------------------- Q4_0, Q5_0, Q8_0 (Q8_0 x)
+
+def _q32_weights(g, wtype, M, K):
+    if wtype == Q.QMM_Q5_0:
+        return synth.q5_0_random(g, M, K)
+    return O.quantize({Q.QMM_Q4_0: O.Q4_0, Q.QMM_Q8_0: O.Q8_0}[wtype], synth.normal_f32(g, (M, K), 0.02))
+
+
+@pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
+@pytest.mark.parametrize("M,N,K", [(32, 64, 128), (1, 9, 32), (31, 65, 96), (130, 100, 896), (300, 129, 1024),
+                                   (128, 512, 2048), (77, 1, 160)])
+def test_gemm_q32_shapes(wtype, M, N, K):
+    g = np.random.default_rng(M * 11 + N * 3 + K + wtype)
+    W = _q32_weights(g, wtype, M, K)
+    xq = O.quantize(O.Q8_0, g.standard_normal((N, K), dtype=np.float32))
+    print("gemm q32", wtype, M, N, K, flush=True)
+    y = to_cpu(Q.mul_mat(wtype, to_gpu(W), to_gpu(xq), M, N, K, algo=2))
+    ow = {Q.QMM_Q4_0: O.Q4_0, Q.QMM_Q5_0: O.Q5_0, Q.QMM_Q8_0: O.Q8_0}[wtype]
+    y_ref, T = O.mul_mat(ow, W, xq, M, N, K)
+    assert_within_tolerance(y, y_ref, T, what=f"GEMM type {wtype} {M}x{K} N={N}")
+
+
+@pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
+def test_gemm_q32_extremes_and_determinism(wtype):
+    # codes at their extremes, a zero activation row, a large one; two runs
+    # bit-identical and nothing written past y
+    g = np.random.default_rng(50 + wtype)
+    M, N, K = 96, 40, 512
+    W = _q32_weights(g, wtype, M, K)
+    S = {Q.QMM_Q4_0: 18, Q.QMM_Q5_0: 22, Q.QMM_Q8_0: 34}[wtype]
+    bl = W.reshape(M, K // 32, S)
+    bl[:8, :, 2:] = 0xFF
+    bl[8:16, :, 2:] = 0x00 if wtype != Q.QMM_Q8_0 else 0x80
+    x = g.standard_normal((N, K), dtype=np.float32)
+    x[3] = 0
+    x[5] = np.sign(x[5]) * 50.0
+    xq = O.quantize(O.Q8_0, x)
+    Wg, Xg = to_gpu(W), to_gpu(xq)
+    outs = []
+    for _ in range(2):
+        buf = torch.full((N * M + 256,), float("nan"), dtype=torch.float32, device=Wg.device)
+        assert Q.qmm_mul_mat_algo(wtype, Wg, Xg, buf, M, N, K, 2) == Q.QMM_OK
+        b = to_cpu(buf)
+        assert np.all(np.isnan(b[N * M:])), "wrote past the end of y"
+        outs.append(b[:N * M].reshape(N, M))
+    assert np.array_equal(outs[0], outs[1])
+    ow = {Q.QMM_Q4_0: O.Q4_0, Q.QMM_Q5_0: O.Q5_0, Q.QMM_Q8_0: O.Q8_0}[wtype]
+    y_ref, T = O.mul_mat(ow, W, xq, M, N, K)
+    assert_within_tolerance(outs[0], y_ref, T, what="q32 extremes")
+    assert np.all(outs[0][3] == 0)
