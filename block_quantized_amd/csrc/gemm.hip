@@ -153,8 +153,11 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.dx[0], 4, vo_dx, (unsigned)sbB, 0, 0);
     };
     // ---- weights: header + this lane's halves of the four nibble-pair chunks
-    uint4 wh, wq[4];
+    // two super-blocks of weights in flight (the next and the one after): one
+    // super-block of compute does not cover a load from HBM
+    uint4 wh, wq[4], wh2, wq2[4];
     auto w_load = [&](int sb, uint4& hdr, uint4 (&q)[4]) {
+        sb = min(sb, SB - 1);  // past the end: a harmless repeat of the last super-block
         const uint8_t* b = wrow + (int64_t)sb * kQ4_KBytes;
         hdr = reinterpret_cast<const uint4*>(b)[0];
 #pragma unroll
@@ -173,10 +176,14 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
         uint4 q[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) q[g] = wq[g];
-        if (sb + 1 < SB) {
-            x_copy(Tn, sb + 1);
-            w_load(sb + 1, wh, wq);
-        }
+        wh = wh2;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) wq[g] = wq2[g];
+        // the activation copy goes first: loads retire in order, and the
+        // barrier that ends this super-block waits for the copy but not for
+        // the weights of super-block sb + 2 issued after it
+        if (sb + 1 < SB) x_copy(Tn, sb + 1);
+        w_load(sb + 2, wh2, wq2);
         const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
         const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
         const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
@@ -238,8 +245,9 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
         __syncthreads();  // the next tile has landed (waits for the copies) and this one is free
     };
 
-    x_copy(tile0, 0);
     w_load(0, wh, wq);
+    x_copy(tile0, 0);
+    w_load(1, wh2, wq2);
     __syncthreads();
     // (each arm names its tiles statically, which is what lets the compiler
     // tell the two apart)

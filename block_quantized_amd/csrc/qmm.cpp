@@ -36,6 +36,19 @@ int check_dims(int t, int64_t rows, int64_t K) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 
+// Largest N for which the automatic choice keeps the GEMV kernels: the
+// crossovers measured on MI355X (4096-wide rows).  The GEMV reads W once per
+// 8 activation rows; the GEMM once per 64, with a fixed cost per super-block
+// or block that the Q4_0/Q5_0/Q8_0 kernels' per-block scaling makes large.
+int64_t gemm_min_rows(int wtype) {
+    switch (wtype) {
+    case QMM_Q6_K: return 8;
+    case QMM_Q4_K: return 16;
+    case QMM_Q4_0: case QMM_Q8_0: return 64;
+    default: return 96;  // Q5_0
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,7 +107,7 @@ int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y, int64_t
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool has_gemm = gemm_supported(wtype);
     if (algo == 2 && !has_gemm) return QMM_ERR_UNSUPPORTED;
-    const bool gemm = algo == 2 || (algo == 0 && N > 8 && has_gemm);
+    const bool gemm = algo == 2 || (algo == 0 && has_gemm && N > gemm_min_rows(wtype));
     return hip_status(gemm ? launch_gemm(wtype, W, xq, y, M, N, K, s) : launch_gemv(wtype, W, xq, y, M, N, K, s));
 }
 

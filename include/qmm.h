@@ -139,17 +139,18 @@ int qmm_dequantize(int type, const void* blocks, float* out, int64_t rows, int64
  *   y     : device, N x M fp32, written (y[n*M + m])
  * Per block: an exact integer dot product of the quants, then the block's
  * float scales; Q4_K and Q6_K take their min and offset terms from the Q8_K
- * block's 16-wide sums.  Accumulation is fp32.  N <= 8 runs the
- * bandwidth-bound GEMV kernels; larger N runs the int8-MFMA GEMM kernels
- * where the weight type has one (Q4_K, Q6_K), else the GEMV kernels in
- * groups of up to 8 activation rows. */
+ * block's 16-wide sums.  Accumulation is fp32.  Small N runs the
+ * bandwidth-bound GEMV kernels (in groups of up to 8 activation rows), larger
+ * N the int8-MFMA GEMM kernels; the switch is at the crossover measured on
+ * MI355X: N > 8 for Q6_K, N > 16 for Q4_K, N > 64 for Q4_0 and Q8_0, N > 96
+ * for Q5_0. */
 int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y,
                 int64_t M, int64_t N, int64_t K, void* stream);
 
 /* qmm_mul_mat with the kernel family chosen by the caller:
  *   algo 0 = automatic (as qmm_mul_mat), 1 = GEMV kernels (any N, run in
- *   column groups of at most 8), 2 = int8-MFMA GEMM kernels (any N; Q4_K
- *   and Q6_K, QMM_ERR_UNSUPPORTED for the other weight types).
+ *   column groups of at most 8), 2 = int8-MFMA GEMM kernels (any N, every
+ *   weight type).
  * Results of the two families agree to float summation order.  Any other
  * algo value returns QMM_ERR_UNSUPPORTED. */
 int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y,
