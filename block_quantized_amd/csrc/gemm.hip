@@ -237,8 +237,8 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * qd + e;
                     const int u = ahi[t][r] * 8 + alo[t][r];
-                    const float v = (float)u * d - dmin * amin[r];
-                    yacc[t][r] += v * dxa[e];
+                    const float v = __builtin_fmaf((float)u, d, -(dmin * amin[r]));
+                    yacc[t][r] = __builtin_fmaf(v, dxa[e], yacc[t][r]);
                 }
             }
         }
