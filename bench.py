@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--quick", action="store_true", help="headline only (no secondary workloads)")
+    p.add_argument("--only", metavar="PREFIX",
+                   help="run only the secondary workloads whose name starts with PREFIX (for profiling; "
+                        "prints their results, not the headline line)")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="summarise PMC counter runs (no GPU needed) and exit")
     return p.parse_args()
@@ -340,36 +343,44 @@ def kv_cache_workloads(b: Bench, reps=20):
     return out
 
 
-def secondary(b: Bench):
+def secondary(b: Bench, only=None):
+    """The other workloads; `only` keeps those whose name starts with it."""
     import oracle as O
     import synth
     out = {}
+    want = lambda name: only is None or name.startswith(only)
     q80 = lambda g, M, K: O.quantize(O.Q8_0, synth.normal_f32(g, (M, K), 0.02))
-    out["q8_0_gemv_2048x2048_b1"] = gemv_workload(b, b.Q.QMM_Q8_0, 2048, 2048, 1, q80)
-    progress("q8_0 gemv done")
+    if want("q8_0_gemv_2048x2048_b1"):
+        out["q8_0_gemv_2048x2048_b1"] = gemv_workload(b, b.Q.QMM_Q8_0, 2048, 2048, 1, q80)
+        progress("q8_0 gemv done")
     for (M, K) in synth.LLAMA_8B_SHAPES:
         for N in (1, 4, 8):
-            out[f"q4_k_gemv_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q4_K, M, K, N, synth.q4_k_random)
-            progress(f"q4_k gemv {M}x{K} b{N} done")
+            if want(f"q4_k_gemv_{M}x{K}_b{N}"):
+                out[f"q4_k_gemv_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q4_K, M, K, N, synth.q4_k_random)
+                progress(f"q4_k gemv {M}x{K} b{N} done")
     M, K = synth.LLAMA_8B_HEAD
     for N in (1, 32):
-        out[f"q6_k_head_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q6_K, M, K, N, synth.q6_k_random,
-                                                     min_bytes=1, reps_floor=20)
-        progress(f"q6_k head b{N} done")
+        if want(f"q6_k_head_{M}x{K}_b{N}"):
+            out[f"q6_k_head_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q6_K, M, K, N, synth.q6_k_random,
+                                                         min_bytes=1, reps_floor=20)
+            progress(f"q6_k head b{N} done")
     for M in (4096, 14336):
-        r = gemv_workload(b, b.Q.QMM_Q4_K, M, 4096, 512, synth.q4_k_random, min_bytes=1, reps_floor=5)
-        r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
-        out[f"q4_k_gemm_{M}x4096_b512"] = r
-        progress(f"q4_k gemm {M}x4096 b512 {r['tops']:.1f} TOPS")
+        if want(f"q4_k_gemm_{M}x4096_b512"):
+            r = gemv_workload(b, b.Q.QMM_Q4_K, M, 4096, 512, synth.q4_k_random, min_bytes=1, reps_floor=5)
+            r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
+            out[f"q4_k_gemm_{M}x4096_b512"] = r
+            progress(f"q4_k gemm {M}x4096 b512 {r['tops']:.1f} TOPS")
     for name, wt, mk in (("q4_0", b.Q.QMM_Q4_0, lambda g, M, K: O.quantize(O.Q4_0, synth.normal_f32(g, (M, K), 0.02))),
                          ("q5_0", b.Q.QMM_Q5_0, synth.q5_0_random),
                          ("q8_0", b.Q.QMM_Q8_0, lambda g, M, K: O.quantize(O.Q8_0, synth.normal_f32(g, (M, K), 0.02)))):
-        r = gemv_workload(b, wt, 4096, 4096, 512, mk, min_bytes=1, reps_floor=5)
-        r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
-        out[f"{name}_gemm_4096x4096_b512"] = r
-        progress(f"{name} gemm 4096x4096 b512 {r['tops']:.1f} TOPS")
-    out.update(kv_cache_workloads(b))
-    progress("kv cache q8_0 done")
+        if want(f"{name}_gemm_4096x4096_b512"):
+            r = gemv_workload(b, wt, 4096, 4096, 512, mk, min_bytes=1, reps_floor=5)
+            r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
+            out[f"{name}_gemm_4096x4096_b512"] = r
+            progress(f"{name} gemm 4096x4096 b512 {r['tops']:.1f} TOPS")
+    if want("kv_q8_0"):
+        out.update(kv_cache_workloads(b))
+        progress("kv cache q8_0 done")
     return out
 
 
@@ -453,6 +464,11 @@ def main():
               "rows with no exchange, so N GPUs would each run this workload on M/N rows.", file=sys.stderr)
         sys.exit(2)
     b = Bench()
+    if a.only:
+        sec = secondary(b, a.only)
+        print(json.dumps({k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                          for k, v in sec.items()}))
+        return
     copy = copy_reference(b)
     progress(f"copy reference {copy['gbs_read_plus_write']} GB/s")
     head, cpu_f32 = decode_sweep(b, a.steps, a.warmup, keep_cpu_layers=0 if a.no_cpu else 2)
