@@ -53,6 +53,7 @@ typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 // 8 and 16 bytes at a 4-byte-aligned address (Q8_K blocks are 292 bytes)
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -608,6 +609,145 @@ __global__ __launch_bounds__(256, 2) void gemm_q32_kernel(const uint8_t* __restr
     }
 }
 
+// ------------------------------------------------------------ narrow batches
+// N <= 32 activation rows (decode batches): one 32-wide MFMA column tile.
+// The weights are streamed once and the kernel aims at HBM bandwidth: a
+// workgroup of 8 waves owns 32 weight rows, wave w takes super-blocks w,
+// w + 8, ..., and the 8 partial tiles are summed in LDS in a fixed order.
+// Compared with the VALU GEMV, the weight decode (scale planes) is shared by
+// all N columns instead of repeated per column.
+//
+// Orientation: the MFMA computes W-row x activation-row tiles (A = weight
+// planes, B = activation codes), so a lane's result column is activation row
+// c, with its scale dx per lane, and its 16 result registers are weight rows
+// 8(r/4) + 4h + r%4, whose d and dmin come from the lanes that loaded those
+// rows, through LDS.  Operands and registers follow the layout used above.
+// Loads for the next super-block of a wave are issued before the current
+// one is computed (two register stages, named statically).  Past the end a
+// wave re-loads its last super-block, which it then skips.
+constexpr int kNarrowWaves = 8;
+
+__global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow_q4k_kernel(const uint8_t* __restrict__ W,
+                                                                       const uint8_t* __restrict__ X,
+                                                                       float* __restrict__ Y, int M, int N,
+                                                                       int SB) {
+    __shared__ __attribute__((aligned(16))) float s_d[kNarrowWaves][2][32];         // d, dmin of the 32 rows
+    __shared__ __attribute__((aligned(16))) float s_part[kNarrowWaves][32][33];     // partial y[n][m]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 31, h = lane >> 5;
+    const int m0 = blockIdx.x * 32;
+    const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
+    const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
+    const int rowsB = SB * kQ8_KBytes;
+    // activation rows past N read as zeros (their outputs are not stored)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(X), (short)0,
+                                                                         N * rowsB, kBufferWord3);
+    const int vo_code = c * rowsB + 4 + 16 * h;  // chunk 2j + h of row c at + 32 j
+    const int vo_sum = c * rowsB + 260 + 16 * h;  // sums 8h .. 8h+7 of row c
+    const int vo_dx = c * rowsB;
+
+    struct Stage {
+        uint4 wh, wq[4];
+        u32x4 xa[8], bsum;
+        uint32_t dx;
+    };
+    auto load = [&](Stage& st, int sb) {
+        sb = min(sb, SB - 1);
+        const uint8_t* b = wrow + (int64_t)sb * kQ4_KBytes;
+        st.wh = reinterpret_cast<const uint4*>(b)[0];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) st.wq[g] = reinterpret_cast<const uint4*>(b + 16 + 32 * g + 16 * h)[0];
+        const int so = sb * kQ8_KBytes;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, vo_code + 32 * j, so, 0);
+        st.bsum = __builtin_amdgcn_raw_buffer_load_b128(xr, vo_sum, so, 0);
+        st.dx = __builtin_amdgcn_raw_buffer_load_b32(xr, vo_dx, so, 0);
+    };
+
+    float yacc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) yacc[r] = 0.f;
+
+    auto compute = [&](const Stage& st) {
+        const uint4 hdr = st.wh;
+        const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
+        const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
+        const uint32_t m47 = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
+        if (h == 0) {  // this lane's row's scales, for the lanes whose registers hold that row
+            s_d[wave][0][c] = h2f(hdr.x);
+            s_d[wave][1][c] = h2f(hdr.x >> 16);
+        }
+        v16i ahi = {}, alo = {};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint4 qq = st.wq[j >> 1];
+            const int shift = (j & 1) * 4;
+            const uint32_t scw = (j < 4) ? sc03 : sc47;
+            const uint32_t sc = (scw >> (8 * (j & 3))) & 0xFF;
+            const uint32_t sh = sc >> 3, sl = sc & 7;
+            const uint32_t q0 = (qq.x >> shift) & 0x0F0F0F0Fu, q1 = (qq.y >> shift) & 0x0F0F0F0Fu;
+            const uint32_t q2 = (qq.z >> shift) & 0x0F0F0F0Fu, q3 = (qq.w >> shift) & 0x0F0F0F0Fu;
+            const v4i bh = {(int)mul_bytes(q0, sh), (int)mul_bytes(q1, sh), (int)mul_bytes(q2, sh), (int)mul_bytes(q3, sh)};
+            const v4i bl = {(int)mul_bytes(q0, sl), (int)mul_bytes(q1, sl), (int)mul_bytes(q2, sl), (int)mul_bytes(q3, sl)};
+            const v4i a = __builtin_bit_cast(v4i, st.xa[j]);
+            ahi = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh, a, ahi, 0, 0, 0);
+            alo = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl, a, alo, 0, 0, 0);
+        }
+        // min term: A = mins of the weight rows (K half h: mins 4h..4h+3 twice
+        // each), B = the activation rows' 16-wide sums 8h..8h+7
+        const uint32_t mw = h ? m47 : m03;
+        v8h mins, bs;
+        const v8s bi = __builtin_bit_cast(v8s, st.bsum);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            mins[e] = (_Float16)(float)((mw >> (8 * (e >> 1))) & 0xFF);
+            bs[e] = (_Float16)bi[e];  // exact: |s| <= 2032
+        }
+        const v16f amin = __builtin_amdgcn_mfma_f32_32x32x16_f16(mins, bs, (v16f){}, 0, 0, 0);
+        const float dx = __uint_as_float(st.dx);
+        // y[n][m] += dx_n * (d_m * (8 P_hi + P_lo) - dmin_m * Smin), m = 8(r/4) + 4h + r%4
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const float4 dd = *reinterpret_cast<const float4*>(&s_d[wave][0][8 * qd + 4 * h]);
+            const float4 dm = *reinterpret_cast<const float4*>(&s_d[wave][1][8 * qd + 4 * h]);
+            const float da[4] = {dd.x, dd.y, dd.z, dd.w}, ma[4] = {dm.x, dm.y, dm.z, dm.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * qd + e;
+                const float u = (float)(ahi[r] * 8 + alo[r]);
+                const float v = __builtin_fmaf(u, da[e], -(ma[e] * amin[r]));
+                yacc[r] = __builtin_fmaf(v, dx, yacc[r]);
+            }
+        }
+    };
+
+    Stage s0, s1;
+    int sb = wave;
+    load(s0, sb);
+    load(s1, sb + kNarrowWaves);
+    for (; sb < SB; sb += 2 * kNarrowWaves) {
+        compute(s0);
+        load(s0, sb + 2 * kNarrowWaves);
+        if (sb + kNarrowWaves < SB) compute(s1);
+        load(s1, sb + 3 * kNarrowWaves);
+    }
+
+    // sum the waves' partial tiles in a fixed order
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_part[wave][c][8 * (r >> 2) + 4 * h + (r & 3)] = yacc[r];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 1024 / (64 * kNarrowWaves); ++k) {
+        const int idx = tid + 64 * kNarrowWaves * k;
+        const int n = idx >> 5, mm = idx & 31;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNarrowWaves; ++w) acc += s_part[w][n][mm];
+        if (n < N && m0 + mm < M) Y[(int64_t)n * M + m0 + mm] = acc;
+    }
+}
+
 }  // namespace
 
 bool gemm_supported(int wtype) {
@@ -649,6 +789,11 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
             hipLaunchKernelGGL(gemm_q6k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
                                (int)mblocks, (int)nb);
         }
+        return hipGetLastError();
+    }
+    if (N <= 32) {
+        hipLaunchKernelGGL(gemm_narrow_q4k_kernel, dim3((unsigned)((M + 31) / 32)), dim3(64 * kNarrowWaves), 0, s, w, x,
+                           y, (int)M, (int)N, SB);
         return hipGetLastError();
     }
     // 64 activation rows per workgroup: two waves per SIMD fit (the 128-row

@@ -37,13 +37,14 @@ int check_dims(int t, int64_t rows, int64_t K) {
 int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 
 // Largest N for which the automatic choice keeps the GEMV kernels: the
-// crossovers measured on MI355X (4096-wide rows).  The GEMV reads W once per
-// 8 activation rows; the GEMM once per 64, with a fixed cost per super-block
-// or block that the Q4_0/Q5_0/Q8_0 kernels' per-block scaling makes large.
+// crossovers measured on MI355X (4096- and 14336-wide rows).  The GEMV
+// decodes the weights once per activation row; the MFMA kernels once per 32
+// or 64 rows, with a fixed cost per super-block or block that the Q4_0, Q5_0
+// and Q8_0 kernels' per-block scaling makes large.
 int64_t gemm_min_rows(int wtype) {
     switch (wtype) {
     case QMM_Q6_K: return 8;
-    case QMM_Q4_K: return 16;
+    case QMM_Q4_K: return 7;
     case QMM_Q4_0: case QMM_Q8_0: return 64;
     default: return 96;  // Q5_0
     }

@@ -83,6 +83,37 @@ def test_gemm_deterministic_and_in_bounds():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("M,N,K", [(33, 1, 2816), (100, 7, 2304), (4096, 32, 4096), (17, 31, 14336),
+                                   (64, 2, 256), (4131, 16, 2048)])
+def test_gemm_q4k_narrow(M, N, K):
+    # N <= 32 runs the narrow kernel: the super-blocks are split over 8 waves
+    # (K/256 = 11, 9, 16, 56, 1, 8 super-blocks: some waves get none) and the
+    # partial tiles are summed in LDS
+    g = np.random.default_rng(M * 3 + N * 5 + K)
+    W = synth.q4_k_random(g, M, K)
+    xq = O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32))
+    print("narrow", M, N, K, flush=True)
+    y = run(W, xq, M, N, K)
+    y_ref, T = O.mul_mat(O.Q4_K, W, xq, M, N, K)
+    assert_within_tolerance(y, y_ref, T, what=f"narrow {M}x{K} N={N}")
+
+
+def test_gemm_q4k_narrow_deterministic_and_in_bounds():
+    g = np.random.default_rng(12)
+    M, N, K = 1000, 20, 3328
+    W = to_gpu(synth.q4_k_random(g, M, K))
+    xq = to_gpu(O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32)))
+    outs = []
+    for _ in range(3):
+        buf = torch.full((N * M + 512,), float("nan"), dtype=torch.float32, device=W.device)
+        assert Q.qmm_mul_mat_algo(Q.QMM_Q4_K, W, xq, buf, M, N, K, 2) == Q.QMM_OK
+        b = to_cpu(buf)
+        assert np.all(np.isnan(b[N * M:])), "wrote past the end of y"
+        assert not np.any(np.isnan(b[:N * M]))
+        outs.append(b[:N * M].view(np.uint32).copy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
 # ------------------------------------------------------------------ Q6_K
 
 def run_q6k(W, xq, M, N, K, algo=2):
