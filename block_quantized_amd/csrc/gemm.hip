@@ -612,8 +612,8 @@ __global__ __launch_bounds__(256, 2) void gemm_q32_kernel(const uint8_t* __restr
 // ------------------------------------------------------------ narrow batches
 // N <= 32 activation rows (decode batches): one 32-wide MFMA column tile.
 // The weights are streamed once and the kernel aims at HBM bandwidth: a
-// workgroup of 8 waves owns 32 weight rows, wave w takes super-blocks w,
-// w + 8, ..., and the 8 partial tiles are summed in LDS in a fixed order.
+// workgroup of NW waves owns 32 weight rows, wave w takes super-blocks w,
+// w + NW, ..., and the NW partial tiles are summed in LDS in a fixed order.
 // Compared with the VALU GEMV, the weight decode (scale planes) is shared by
 // all N columns instead of repeated per column.
 //
@@ -625,8 +625,7 @@ __global__ __launch_bounds__(256, 2) void gemm_q32_kernel(const uint8_t* __restr
 // Loads for the next super-block of a wave are issued before the current
 // one is computed (two register stages, named statically).  Past the end a
 // wave re-loads its last super-block, which it then skips.
-constexpr int kNarrowWaves = 8;
-
+template <int kNarrowWaves>
 __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow_q4k_kernel(const uint8_t* __restrict__ W,
                                                                        const uint8_t* __restrict__ X,
                                                                        float* __restrict__ Y, int M, int N,
@@ -792,8 +791,15 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         return hipGetLastError();
     }
     if (N <= 32) {
-        hipLaunchKernelGGL(gemm_narrow_q4k_kernel, dim3((unsigned)((M + 31) / 32)), dim3(64 * kNarrowWaves), 0, s, w, x,
-                           y, (int)M, (int)N, SB);
+        // 8 waves per workgroup (one workgroup per CU) while the row tiles fit
+        // in one pass over the CUs; past that, 4 (two workgroups per CU)
+        const int64_t tiles = (M + 31) / 32;
+        if (tiles <= 256)
+            hipLaunchKernelGGL(gemm_narrow_q4k_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, s, w, x, y, (int)M,
+                               (int)N, SB);
+        else
+            hipLaunchKernelGGL(gemm_narrow_q4k_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, s, w, x, y, (int)M,
+                               (int)N, SB);
         return hipGetLastError();
     }
     // 64 activation rows per workgroup: two waves per SIMD fit (the 128-row

@@ -41,10 +41,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 // decodes the weights once per activation row; the MFMA kernels once per 32
 // or 64 rows, with a fixed cost per super-block or block that the Q4_0, Q5_0
 // and Q8_0 kernels' per-block scaling makes large.
-int64_t gemm_min_rows(int wtype) {
+int64_t gemm_min_rows(int wtype, int64_t M) {
     switch (wtype) {
     case QMM_Q6_K: return 8;
-    case QMM_Q4_K: return 7;
+    case QMM_Q4_K: return M > 256 * 32 ? 3 : 7;  // the narrow kernel's two-workgroups-per-CU form wins from N = 4
     case QMM_Q4_0: case QMM_Q8_0: return 64;
     default: return 96;  // Q5_0
     }
@@ -108,7 +108,7 @@ int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y, int64_t
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool has_gemm = gemm_supported(wtype);
     if (algo == 2 && !has_gemm) return QMM_ERR_UNSUPPORTED;
-    const bool gemm = algo == 2 || (algo == 0 && has_gemm && N > gemm_min_rows(wtype));
+    const bool gemm = algo == 2 || (algo == 0 && has_gemm && N > gemm_min_rows(wtype, M));
     return hip_status(gemm ? launch_gemm(wtype, W, xq, y, M, N, K, s) : launch_gemv(wtype, W, xq, y, M, N, K, s));
 }
 
