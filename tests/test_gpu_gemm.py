@@ -122,8 +122,7 @@ def run_q6k(W, xq, M, N, K, algo=2):
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 256), (1, 9, 256), (31, 33, 512), (130, 100, 768), (300, 32, 2048),
                                    (129, 65, 256), (77, 1, 256), (4100, 32, 4096), (64, 8, 1280),
-                                   # N <= 32: the narrow kernel, 8 waves (<= 256 row tiles) or 4, and
-                                   # 11 / 9 / 4 super-blocks spread over them
+                                   # N <= 32 with 11 / 9 / 4 super-blocks per row and ragged M
                                    (33, 5, 2816), (9000, 17, 2304), (8200, 31, 1024)])
 def test_gemm_q6k_shapes(M, N, K):
     g = np.random.default_rng(M * 5 + N * 17 + K)
