@@ -577,8 +577,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     const int TW = gridDim.x * wpg;
     const int P = 1 << logP;
     // lane's place inside a chunk
-    const int lr = NKC == 1 ? lane >> logP : 0;
-    const int lg = NKC == 1 ? lane & (P - 1) : lane;
+    const int lr = lane >> logP;
+    const int lg = lane & (P - 1);
     const bool lwriter = (lane & (P - 1)) == 0 && lr < RW;
 
     // Where this lane's unit lies.
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
             w0 = in ? sW0[k] : w0;
         }
         const int64_t row0 = (wi - w0) * RW;  // uniform
-        const int gu = kc * 64 + lg;  // kc is 0 when a row fits one chunk
+        const int gu = kc * P + lg;  // kc is 0 when a row fits one chunk
         const int64_t row = row0 + lr;
         const bool valid = gu < GU && lr < RW && row < M;
         L.valid = valid;
@@ -894,8 +894,8 @@ hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const i
     int logP = 0;
     while ((1 << logP) < Pl) ++logP;
     a.logP = logP;
-    a.RW = a.GU >= 64 ? 1 : 64 >> logP;
-    a.nkc = (a.GU + 63) / 64;
+    a.RW = 64 >> logP;
+    a.nkc = (a.GU + (1 << logP) - 1) >> logP;
     int64_t work = 0;
     for (int i = 0; i < nseg; ++i) {
         a.seg[i].W = static_cast<const uint8_t*>(Ws[i]);

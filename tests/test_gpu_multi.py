@@ -50,7 +50,9 @@ def test_multi_fused_matches_separate_and_oracle(wt, K, Ms, N):
     multi_q = [to_cpu(y) for y in Q.mul_mat_multi(wt, Wg, Ms, xq_gpu, N, K, x_is_f32=False)]
     xq = O.quantize(xt, x)
     for i, (W, M) in enumerate(zip(Ws, Ms)):
-        single = to_cpu(Q.mul_mat(wt, Wg[i], xq_gpu, M, N, K))
+        # the multi launch runs the GEMV kernels: compare with the same kernels
+        # run one matrix at a time (algo 1), bit for bit
+        single = to_cpu(Q.mul_mat(wt, Wg[i], xq_gpu, M, N, K, algo=1))
         assert np.array_equal(fused[i].view(np.uint32), single.view(np.uint32)), f"fused != single (matrix {i})"
         assert np.array_equal(multi_q[i].view(np.uint32), single.view(np.uint32)), f"multi != single (matrix {i})"
         y_ref, T = O.mul_mat(wt, W, xq, M, N, K)
