@@ -54,6 +54,9 @@ typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -747,6 +750,134 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow_q4k_kernel(cons
     }
 }
 
+// N <= 16 with few weight rows (M <= 8192): the same kernel on 16-row tiles,
+// twice as many workgroups.  v_mfma_i32_16x16x64_i8 (checked on the
+// hardware): lane l gives row l%16 of A and column l%16 of B, k = 16(l/16)
+// .. +15 of each 64-value group, and receives column l%16, rows 4(l/16)+i of
+// the result; v_mfma_f32_16x16x16_f16 is the same with k = 4(l/16) .. +3.
+// With the sub-block scales inside the planes, the four K quarters of a
+// 64-value group may come from two sub-blocks.  Lane (r, q) = (l%16, l/16)
+// takes, of 64-value group g, the 16 values 64g + 16q ..: the low (q < 2) or
+// high (q >= 2) nibbles of qs[32g + 16(q&1) ..], of sub-block 2g + q/2.
+template <int kNarrowWaves>
+__global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow16_q4k_kernel(const uint8_t* __restrict__ W,
+                                                                         const uint8_t* __restrict__ X,
+                                                                         float* __restrict__ Y, int M, int N,
+                                                                         int SB) {
+    __shared__ __attribute__((aligned(16))) float s_d[kNarrowWaves][2][16];      // d, dmin of the 16 rows
+    __shared__ __attribute__((aligned(16))) float s_part[kNarrowWaves][16][17];  // partial y[n][m]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, q = lane >> 4;
+    const int m0 = blockIdx.x * 16;
+    const int mrow = min(m0 + r, M - 1);  // rows past M are computed on a copy and not stored
+    const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
+    const int rowsB = SB * kQ8_KBytes;
+    // activation rows past N read as zeros (their outputs are not stored)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(X), (short)0,
+                                                                         N * rowsB, kBufferWord3);
+    const int vo_code = r * rowsB + 4 + 16 * q;  // values 64g + 16q .. of row r at + 64 g
+    const int vo_sum = r * rowsB + 260 + 8 * q;  // 16-wide sums 4q .. 4q+3 of row r
+    const int vo_dx = r * rowsB;
+    const int qsoff = 16 + 16 * (q & 1);         // this lane's 16 qs bytes of group g at + 32 g
+    const int nsh = (q >> 1) * 4;                // low or high nibbles
+
+    struct Stage {
+        uint4 wh, wq[4];
+        u32x4 xa[4];
+        uint32_t bsum[2], dx;
+    };
+    auto load = [&](Stage& st, int sb) {
+        sb = min(sb, SB - 1);
+        const uint8_t* b = wrow + (int64_t)sb * kQ4_KBytes;
+        st.wh = reinterpret_cast<const uint4*>(b)[0];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) st.wq[g] = reinterpret_cast<const uint4*>(b + qsoff + 32 * g)[0];
+        const int so = sb * kQ8_KBytes;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) st.xa[g] = __builtin_amdgcn_raw_buffer_load_b128(xr, vo_code + 64 * g, so, 0);
+        const u32x2 bs = __builtin_amdgcn_raw_buffer_load_b64(xr, vo_sum, so, 0);
+        st.bsum[0] = bs.x;
+        st.bsum[1] = bs.y;
+        st.dx = __builtin_amdgcn_raw_buffer_load_b32(xr, vo_dx, so, 0);
+    };
+
+    float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const Stage& st) {
+        const uint4 hdr = st.wh;
+        const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
+        const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
+        const uint32_t m47 = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
+        if (q == 0) {  // this lane's row's scales, for the lanes whose registers hold that row
+            s_d[wave][0][r] = h2f(hdr.x);
+            s_d[wave][1][r] = h2f(hdr.x >> 16);
+        }
+        v4i ahi = {}, alo = {};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint4 qq = st.wq[g];
+            const int j = 2 * g + (q >> 1);  // sub-block of this lane's 16 values
+            const uint32_t scw = (g < 2) ? sc03 : sc47;
+            const uint32_t sc = (scw >> (8 * (j & 3))) & 0xFF;
+            const uint32_t sh = sc >> 3, sl = sc & 7;
+            const uint32_t q0 = (qq.x >> nsh) & 0x0F0F0F0Fu, q1 = (qq.y >> nsh) & 0x0F0F0F0Fu;
+            const uint32_t q2 = (qq.z >> nsh) & 0x0F0F0F0Fu, q3 = (qq.w >> nsh) & 0x0F0F0F0Fu;
+            const v4i bh = {(int)mul_bytes(q0, sh), (int)mul_bytes(q1, sh), (int)mul_bytes(q2, sh), (int)mul_bytes(q3, sh)};
+            const v4i bl = {(int)mul_bytes(q0, sl), (int)mul_bytes(q1, sl), (int)mul_bytes(q2, sl), (int)mul_bytes(q3, sl)};
+            const v4i a = __builtin_bit_cast(v4i, st.xa[g]);
+            ahi = __builtin_amdgcn_mfma_i32_16x16x64_i8(bh, a, ahi, 0, 0, 0);
+            alo = __builtin_amdgcn_mfma_i32_16x16x64_i8(bl, a, alo, 0, 0, 0);
+        }
+        // min term: A = mins of the weight rows (slots 4q .. 4q+3 are
+        // sub-blocks 2q, 2q, 2q+1, 2q+1), B = the activation rows' sums
+        const uint32_t mw = (q < 2) ? m03 : m47;
+        const int mi = 2 * (q & 1);  // first of this lane's two mins within mw
+        v4h mins, bs;
+        mins[0] = mins[1] = (_Float16)(float)((mw >> (8 * mi)) & 0xFF);
+        mins[2] = mins[3] = (_Float16)(float)((mw >> (8 * mi + 8)) & 0xFF);
+        bs[0] = (_Float16)(float)(int16_t)(st.bsum[0] & 0xFFFF);  // exact: |s| <= 2032
+        bs[1] = (_Float16)(float)(int16_t)(st.bsum[0] >> 16);
+        bs[2] = (_Float16)(float)(int16_t)(st.bsum[1] & 0xFFFF);
+        bs[3] = (_Float16)(float)(int16_t)(st.bsum[1] >> 16);
+        const v4f amin = __builtin_amdgcn_mfma_f32_16x16x16f16(mins, bs, (v4f){}, 0, 0, 0);
+        const float dx = __uint_as_float(st.dx);
+        // y[n][m] += dx_n * (d_m * (8 P_hi + P_lo) - dmin_m * Smin), m = 4q + i
+        const float4 dd = *reinterpret_cast<const float4*>(&s_d[wave][0][4 * q]);
+        const float4 dm = *reinterpret_cast<const float4*>(&s_d[wave][1][4 * q]);
+        const float da[4] = {dd.x, dd.y, dd.z, dd.w}, ma[4] = {dm.x, dm.y, dm.z, dm.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float u = (float)(ahi[i] * 8 + alo[i]);
+            const float v = __builtin_fmaf(u, da[i], -(ma[i] * amin[i]));
+            yacc[i] = __builtin_fmaf(v, dx, yacc[i]);
+        }
+    };
+
+    Stage s0, s1;
+    int sb = wave;
+    load(s0, sb);
+    load(s1, sb + kNarrowWaves);
+    for (; sb < SB; sb += 2 * kNarrowWaves) {
+        compute(s0);
+        load(s0, sb + 2 * kNarrowWaves);
+        if (sb + kNarrowWaves < SB) compute(s1);
+        load(s1, sb + 3 * kNarrowWaves);
+    }
+
+    // sum the waves' partial tiles in a fixed order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_part[wave][r][4 * q + i] = yacc[i];
+    __syncthreads();
+    if (tid < 256) {
+        const int n = tid >> 4, mm = tid & 15;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNarrowWaves; ++w) acc += s_part[w][n][mm];
+        if (n < N && m0 + mm < M) Y[(int64_t)n * M + m0 + mm] = acc;
+    }
+}
+
 }  // namespace
 
 bool gemm_supported(int wtype) {
@@ -788,6 +919,16 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
             hipLaunchKernelGGL(gemm_q6k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
                                (int)mblocks, (int)nb);
         }
+        return hipGetLastError();
+    }
+    if (N <= 16 && M <= 8192) {  // 16-row tiles: enough workgroups for every CU
+        const int64_t tiles = (M + 15) / 16;
+        if (tiles <= 256)
+            hipLaunchKernelGGL(gemm_narrow16_q4k_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, s, w, x, y, (int)M,
+                               (int)N, SB);
+        else
+            hipLaunchKernelGGL(gemm_narrow16_q4k_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, s, w, x, y, (int)M,
+                               (int)N, SB);
         return hipGetLastError();
     }
     if (N <= 32) {

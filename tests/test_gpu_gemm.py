@@ -84,11 +84,13 @@ def test_gemm_deterministic_and_in_bounds():
 
 
 @pytest.mark.parametrize("M,N,K", [(33, 1, 2816), (100, 7, 2304), (4096, 32, 4096), (17, 31, 14336),
-                                   (64, 2, 256), (4131, 16, 2048)])
+                                   (64, 2, 256), (4131, 16, 2048), (8192, 16, 4096), (4096, 12, 14336),
+                                   (9000, 5, 1024)])
 def test_gemm_q4k_narrow(M, N, K):
-    # N <= 32 runs the narrow kernel: the super-blocks are split over 8 waves
-    # (K/256 = 11, 9, 16, 56, 1, 8 super-blocks: some waves get none) and the
-    # partial tiles are summed in LDS
+    # N <= 32 runs the narrow kernels: the super-blocks are split over the
+    # waves of a workgroup (K/256 = 11, 9, 16, 56, 1, 8, 16, 56, 4 super-blocks:
+    # some waves get none) and the partial tiles are summed in LDS; N <= 16
+    # with M <= 8192 takes 16-row tiles (8 or 4 waves), the rest 32-row tiles
     g = np.random.default_rng(M * 3 + N * 5 + K)
     W = synth.q4_k_random(g, M, K)
     xq = O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32))
@@ -98,9 +100,9 @@ def test_gemm_q4k_narrow(M, N, K):
     assert_within_tolerance(y, y_ref, T, what=f"narrow {M}x{K} N={N}")
 
 
-def test_gemm_q4k_narrow_deterministic_and_in_bounds():
-    g = np.random.default_rng(12)
-    M, N, K = 1000, 20, 3328
+@pytest.mark.parametrize("M,N,K", [(1000, 20, 3328), (1000, 13, 3328)])
+def test_gemm_q4k_narrow_deterministic_and_in_bounds(M, N, K):
+    g = np.random.default_rng(12 + N)
     W = to_gpu(synth.q4_k_random(g, M, K))
     xq = to_gpu(O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32)))
     outs = []
