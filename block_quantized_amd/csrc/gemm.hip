@@ -98,14 +98,26 @@ __device__ __forceinline__ uint32_t mul_bytes(uint32_t v, uint32_t s) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Activation tile of one super-block in LDS: column n's 256 codes at
-// codes[n] (row stride kCodeStride spreads the operand reads over the LDS
-// banks), its 16 sums, its scale.
+// Copies 16 bytes per lane from a buffer into LDS (lane l's bytes land at
+// lds + 16 l) with no VGPR round trip.  The 16-byte form is gfx950's; the
+// host pass of the compiler does not know it, so it sees an empty body.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voff, unsigned soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+// Activation tile of one super-block in LDS: row n's 256 codes as 16 chunks
+// of 16 bytes, chunk q stored at position q ^ (n & 15), so that the operand
+// reads of 16 consecutive rows at one chunk fall on all 64 LDS banks; its 16
+// sums; its scale.  The sums and scales have room for 48 more rows: every
+// wave copies rows past its own share (the same bytes as the wave that owns
+// them), so that all waves issue the same copies with no branch.
 template <int BN>
 struct XTile {
-    uint8_t codes[BN][kCodeStride];
-    int16_t sums[BN][16];
-    float dx[BN];
+    uint8_t codes[BN][256];
+    int16_t sums[BN + 48][16];
+    float dx[BN + 48];
 };
 
 // The activation tile is copied from global memory straight into LDS
@@ -132,29 +144,31 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
     const int n0 = cb * BN;
     const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
     const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
+    const int hsw = h ^ (c & 15);  // chunk 2j + h of row 32t + c sits at position (2j) ^ hsw
 
     // ---- activation copies (per lane: constant offsets; per super-block: scalar offsets)
     const int rowsB = SB * kQ8_KBytes;  // bytes of one activation row
     const int nrows = min(BN, N - n0);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(X) + (int64_t)n0 * rowsB, (short)0, nrows * rowsB, kBufferWord3);
-    const unsigned vo_codes = 4u + 4u * lane;                                   // dword l of the 256 codes
-    const unsigned vo_sums = (unsigned)((lane >> 3) * rowsB + 260 + 4 * (lane & 7));  // 8 rows x 8 dwords
-    const unsigned vo_dx = (unsigned)(lane * rowsB);                            // row l's scale
+    // codes: one instruction moves 4 rows (16 lanes per row, one chunk
+    // each); wave w's instruction i covers rows 4 (w + 4 i) .. +3, whose
+    // swizzle (row & 15) does not depend on i
+    const int crow = 4 * wave + (lane >> 4), cq = lane & 15;
+    const unsigned vo_codes = (unsigned)(crow * rowsB + 4 + 16 * (cq ^ (crow & 15)));
+    // sums and scales: wave w copies rows BN/4 w onward (32 rows of sums, 64
+    // scales), which covers its share of BN/4 rows
+    const unsigned vo_sums = (unsigned)((lane >> 1) * rowsB + 260 + 16 * (lane & 1));  // 32 rows x 2 halves
+    const unsigned vo_dx = (unsigned)(lane * rowsB);                                   // row l's scale
+    static_assert(BN / 4 <= 32 && BN / 4 * 3 + 64 <= BN + 48, "the sums and scales copies fit the tile");
     auto x_copy = [&](XTile<BN>& T, int sb) {
         const int sbB = sb * kQ8_KBytes;
+        const int r0 = BN / 4 * wave;
 #pragma unroll
-        for (int i = 0; i < BN / 4; ++i) {  // rows wave, wave + 4, ...: one instruction per row
-            const int n = wave + 4 * i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.codes[n][0], 4, vo_codes, (unsigned)(n * rowsB + sbB), 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < BN / 32; ++i) {  // sums of rows 8g .. 8g+7 per instruction
-            const int g = wave + 4 * i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.sums[8 * g][0], 4, vo_sums, (unsigned)(8 * g * rowsB + sbB), 0, 0);
-        }
-        if (wave == 0 && lane < BN)  // (BN < 64: the other lanes' copies would fall past the tile)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.dx[0], 4, vo_dx, (unsigned)sbB, 0, 0);
+        for (int i = 0; i < BN / 16; ++i)
+            copy16_to_lds(xr, &T.codes[4 * (wave + 4 * i)][0], vo_codes, (unsigned)(16 * i * rowsB + sbB));
+        copy16_to_lds(xr, &T.sums[r0][0], vo_sums, (unsigned)(r0 * rowsB + sbB));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.dx[r0], 4, vo_dx, (unsigned)(r0 * rowsB + sbB), 0, 0);
     };
     // ---- weights: header + this lane's halves of the four nibble-pair chunks
     // two super-blocks of weights in flight (the next and the one after): one
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
                             (int)mul_bytes(q3, sl)};
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const v4i a = *reinterpret_cast<const v4i*>(&T.codes[32 * t + c][32 * j + 16 * h]);
+                const v4i a = *reinterpret_cast<const v4i*>(&T.codes[32 * t + c][16 * ((2 * j) ^ hsw)]);
                 ahi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bh, ahi[t], 0, 0, 0);
                 alo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bl, alo[t], 0, 0, 0);
             }
