@@ -366,7 +366,7 @@ def secondary(b: Bench, only=None):
     for N in (1, 32):
         if want(f"q6_k_head_{M}x{K}_b{N}"):
             out[f"q6_k_head_{M}x{K}_b{N}"] = gemv_workload(b, b.Q.QMM_Q6_K, M, K, N, synth.q6_k_random,
-                                                         min_bytes=1, reps_floor=20)
+                                                         reps_floor=4)
             progress(f"q6_k head b{N} done")
     for M in (4096, 14336):
         if want(f"q4_k_gemm_{M}x4096_b512"):
