@@ -15,15 +15,18 @@
 // GGUF", "The ggml Tensor Library and Backends": decode speed tracks memory
 // bandwidth), so the kernel is organised around moving W at full HBM rate:
 //
-//  * A lane's unit of work is a run of consecutive weights of one row,
-//    16-byte aligned, loaded by that lane alone with 16-byte loads straight
-//    into registers: 256 weights (8 blocks, 144 B) for Q4_0, 256 (8 blocks,
-//    272 B) for Q8_0, one 144 B super-block for Q4_K, and 8 super-blocks
-//    (1680 B) for Q6_K, whose 210 B super-blocks are only 2-byte aligned:
-//    its j-th super-block starts 2j bytes past a 16-byte boundary, so each
-//    of the 8 sub-steps reads a 224 B window whose skew is a compile-time
-//    constant.  (Measured on MI355X: per-lane 144 B units stream as fast as
-//    fully coalesced reads, ~6.3 TB/s; staging through LDS halved that.)
+//  * A lane's unit of work is 256 consecutive weights of one row, loaded by
+//    that lane alone with 16-byte loads straight into registers: 8 blocks
+//    (144 B) for Q4_0, 8 blocks (272 B) for Q8_0, one 144 B super-block for
+//    Q4_K, one 210 B super-block for Q6_K.  Consecutive lanes take
+//    consecutive units, so a wavefront reads one contiguous run of memory.
+//    Q6_K super-blocks are only 2-byte aligned: a lane reads 208 bytes from
+//    the 4-byte boundary at or below its super-block (13 loads) plus its last
+//    four bytes as two 2-byte loads, and shifts by the 0 or 2 byte skew.
+//    (Measured on MI355X: per-lane 144 B units stream as fast as fully
+//    coalesced reads, ~6.3 TB/s, and so do the 210 B Q6_K units read this
+//    way; 8-super-block Q6_K units per lane, read in 224 B windows, streamed
+//    at 2.4 TB/s in the same probe.  Staging through LDS halved the rate.)
 //  * Loads run one step ahead (two register buffers), and the first step's
 //    loads are issued before the activations are staged.
 //  * A row of K weights is GU units; P = next power of two >= min(GU, 64)
@@ -40,14 +43,17 @@
 namespace qmm {
 namespace {
 
-template <int WT> struct U;
-template <> struct U<QMM_Q4_0> { static constexpr int UB = 144, NV = 9, SUB = 1, WPU = 256; };
-template <> struct U<QMM_Q8_0> { static constexpr int UB = 272, NV = 17, SUB = 1, WPU = 256; };
-template <> struct U<QMM_Q5_0> { static constexpr int UB = 176, NV = 11, SUB = 1, WPU = 256; };
-template <> struct U<QMM_Q4_K> { static constexpr int UB = 144, NV = 9, SUB = 1, WPU = 256; };
-template <> struct U<QMM_Q6_K> { static constexpr int UB = 8 * kQ6_KBytes, NV = 14, SUB = 8, WPU = 2048; };
+// 16 bytes at a 4-byte-aligned address (Q6_K super-blocks are 2-byte aligned)
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-template <int J, int B> struct Tag { static constexpr int j = J, b = B; };
+template <int WT> struct U;
+template <> struct U<QMM_Q4_0> { static constexpr int UB = 144, NV = 9; };
+template <> struct U<QMM_Q8_0> { static constexpr int UB = 272, NV = 17; };
+template <> struct U<QMM_Q5_0> { static constexpr int UB = 176, NV = 11; };
+template <> struct U<QMM_Q4_K> { static constexpr int UB = 144, NV = 9; };
+template <> struct U<QMM_Q6_K> { static constexpr int UB = kQ6_KBytes, NV = 14; };
+
+template <int B> struct Buf { static constexpr int b = B; };  // register buffer B (compile-time)
 
 constexpr int XREC = 336;  // LDS bytes per (activation row, 256-value group)
 constexpr int kMaxSeg = 4;
@@ -502,16 +508,15 @@ __device__ __forceinline__ void unit_q4_k(const uint32_t* w, const uint8_t* xr0,
     }
 }
 
-// One Q6_K super-block whose first byte is byte SKEW of the window r (SKEW
-// even, 0..14): dword i of the super-block is bytes SKEW + 4i .. of r.
-template <int NC, int SKEW>
-__device__ __forceinline__ void unit_q6_k(const uint32_t* r, const uint8_t* xr0, int xstride, float (&acc)[NC]) {
-    constexpr int o = SKEW >> 2;
-    auto W = [&](int i) -> uint32_t {
-        if constexpr ((SKEW & 3) == 0) return r[o + i];
-        else return __builtin_amdgcn_alignbyte(r[o + i + 1], r[o + i], 2);
-    };
-    const float dw = h2f(W(52));
+// One Q6_K super-block.  r[0..51] are the 208 bytes from the 4-byte boundary
+// at or below its first byte, which is byte `skew` (0 or 2) of r; r[52] holds
+// its bytes 206-207 and r[53] its bytes 208-209 (d), each in the low half.
+// Dword i < 52 of the super-block is bytes skew + 4i .. of r.
+template <int NC>
+__device__ __forceinline__ void unit_q6_k(const uint32_t* r, uint32_t skew, const uint8_t* xr0, int xstride,
+                                          float (&acc)[NC]) {
+    auto W = [&](int i) -> uint32_t { return __builtin_amdgcn_alignbyte(r[i + 1], r[i], skew); };
+    const float dw = h2f(r[53]);
     int isum[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) isum[n] = 0;
@@ -550,7 +555,7 @@ __device__ __forceinline__ void unit_q6_k(const uint32_t* r, const uint8_t* xr0,
 template <int WT, int NC, bool XF>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     using F = U<WT>;
-    constexpr int NV = F::NV, SUB = F::SUB;
+    constexpr int NV = F::NV;
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
 
     // Every argument is read once, up front, so the kernel-argument loads form
@@ -623,15 +628,29 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         const int64_t left = M - row0;  // >= 1
         L.nrec = 4 * (int)(left < RW ? left : RW);
         L.yoff = lwriter ? 4 * lr : kNoStore;
-        L.g = gu * (F::WPU / 256);
+        L.g = gu;
         L.last = kc == NKC - 1;
         return L;
     };
-    // Sub-step j of a unit: a window of NV 16-byte pieces.
-    auto load = [&](const Loc& L, int j, uint4 (&v)[NV]) {
-        const uint4* q = reinterpret_cast<const uint4*>(L.p + (SUB > 1 ? ((kQ6_KBytes * j) & ~15) : 0));
+    // A unit's bytes: NV 16-byte pieces (Q6_K: 13 pieces from the 4-byte
+    // boundary at or below the unit, then its last 4 bytes as two halves, so
+    // no byte outside the unit's row is read).
+    auto load = [&](const Loc& L, uint4 (&v)[NV]) {
+        if constexpr (WT == QMM_Q6_K) {
+            const u32x4_a4* q = reinterpret_cast<const u32x4_a4*>(
+                reinterpret_cast<uintptr_t>(L.p) & ~static_cast<uintptr_t>(3));
 #pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = q[i];
+            for (int i = 0; i < NV - 1; ++i) {
+                const u32x4_a4 t = q[i];
+                v[i] = make_uint4(t.x, t.y, t.z, t.w);
+            }
+            const uint16_t* h = reinterpret_cast<const uint16_t*>(L.p);
+            v[NV - 1] = make_uint4(h[103], h[104], 0u, 0u);
+        } else {
+            const uint4* q = reinterpret_cast<const uint4*>(L.p);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) v[i] = q[i];
+        }
     };
 
     uint4 buf[2][NV];
@@ -639,7 +658,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     int64_t nwi = gw;  // position of `nxt`: work item and chunk
     int pkc = 0;
     nxt = locate(gw < nwork ? gw : nwork - 1, 0);
-    stage_x<WT, NC, XF>(xq, G, xl, [&]() { load(nxt, 0, buf[0]); });
+    stage_x<WT, NC, XF>(xq, G, xl, [&]() { load(nxt, buf[0]); });
     __syncthreads();
     if (gw >= nwork) return;  // no barrier follows
 
@@ -648,20 +667,19 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     for (int n = 0; n < NC; ++n) acc[n] = 0.f;
     const int xstride = G * XREC;
 
-    // One sub-step: prefetch the next sub-step into the other buffer, then
-    // compute sub-step J of `cur` from buffer B.  J and B are compile-time.
+    // One step: prefetch the next unit into the other buffer (unless this is
+    // the wave's last), then compute `cur` from buffer B.
     auto step = [&](auto tag, auto more) {
-        constexpr int J = decltype(tag)::j, B = decltype(tag)::b;
-        if constexpr (J + 1 < SUB) load(cur, J + 1, buf[B ^ 1]);
-        else if constexpr (decltype(more)::value) load(nxt, 0, buf[B ^ 1]);
+        constexpr int B = decltype(tag)::b;
+        if constexpr (decltype(more)::value) load(nxt, buf[B ^ 1]);
         if (cur.valid) {
             const uint32_t* w = reinterpret_cast<const uint32_t*>(buf[B]);
-            const uint8_t* xr0 = xl + (cur.g + J) * XREC;
+            const uint8_t* xr0 = xl + cur.g * XREC;
             if constexpr (WT == QMM_Q4_0) unit_q4_0<NC>(w, xr0, xstride, acc);
             else if constexpr (WT == QMM_Q5_0) unit_q5_0<NC>(w, xr0, xstride, acc);
             else if constexpr (WT == QMM_Q8_0) unit_q8_0<NC>(w, xr0, xstride, acc);
             else if constexpr (WT == QMM_Q4_K) unit_q4_k<NC>(w, xr0, xstride, acc);
-            else unit_q6_k<NC, 2 * J>(w, xr0, xstride, acc);  // super-block J starts 2J bytes into its window
+            else unit_q6_k<NC>(w, (uint32_t)reinterpret_cast<uintptr_t>(cur.p) & 3u, xr0, xstride, acc);
         }
     };
     // After the last chunk of a work item: butterfly over the P lanes of
@@ -691,56 +709,37 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
 
     // The last unit of a wave is computed by its own copy of the step, which
     // issues no further load (a uniform branch, taken once per wave).
-    if constexpr (SUB == 1) {
-        for (;;) {
-            if (!advance()) {
-                step(Tag<0, 0>{}, std::false_type{});
-                finish();
-                break;
-            }
-            step(Tag<0, 0>{}, std::true_type{});
+    for (;;) {
+        if (!advance()) {
+            step(Buf<0>{}, std::false_type{});
             finish();
-            if (!advance()) {
-                step(Tag<0, 1>{}, std::false_type{});
-                finish();
-                break;
-            }
-            step(Tag<0, 1>{}, std::true_type{});
-            finish();
+            break;
         }
-    } else {
-        for (;;) {
-            const bool more = advance();
-            step(Tag<0, 0>{}, std::true_type{});
-            step(Tag<1, 1>{}, std::true_type{});
-            step(Tag<2, 0>{}, std::true_type{});
-            step(Tag<3, 1>{}, std::true_type{});
-            step(Tag<4, 0>{}, std::true_type{});
-            step(Tag<5, 1>{}, std::true_type{});
-            step(Tag<6, 0>{}, std::true_type{});
-            if (!more) {
-                step(Tag<7, 1>{}, std::false_type{});
-                finish();
-                break;
-            }
-            step(Tag<7, 1>{}, std::true_type{});
+        step(Buf<0>{}, std::true_type{});
+        finish();
+        if (!advance()) {
+            step(Buf<1>{}, std::false_type{});
             finish();
+            break;
         }
+        step(Buf<1>{}, std::true_type{});
+        finish();
     }
 }
 
 // ------------------------------------------------ shapes the kernel above skips
-// Q4_0 / Q8_0 rows whose K is a multiple of 32 but not of 256, and Q6_K rows
-// whose K is not a multiple of 2048: one wavefront per row, lanes over the
-// blocks, plain 2-byte loads.  Correct for any such shape.
+// Q4_0 / Q5_0 / Q8_0 rows whose K is a multiple of 32 but not of 256: one
+// wavefront per row, lanes over the blocks, plain 2-byte loads.  Correct for
+// any such shape.
 template <int WT>
 __global__ __launch_bounds__(256) void gemv_rowwave_kernel(const uint8_t* __restrict__ W,
                                                            const uint8_t* __restrict__ xq, float* __restrict__ y,
                                                            int64_t M, int N, int64_t K) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    static_assert(WT == QMM_Q4_0 || WT == QMM_Q5_0 || WT == QMM_Q8_0, "32-value block types only");
     if (row >= M) return;
-    if constexpr (WT == QMM_Q4_0 || WT == QMM_Q5_0 || WT == QMM_Q8_0) {
+    {
         constexpr int WB = (WT == QMM_Q4_0) ? kQ4_0Bytes : (WT == QMM_Q5_0) ? kQ5_0Bytes : kQ8_0Bytes;
         const int64_t nb = K / 32;
         for (int n = 0; n < N; ++n) {
@@ -782,34 +781,6 @@ __global__ __launch_bounds__(256) void gemv_rowwave_kernel(const uint8_t* __rest
                         dot = dot4(ld_u16x2_g(wb + 2 + 4 * k), ld_u16x2_g(xb + 2 + 4 * k), dot);
                 }
                 acc += (float)dot * (dw * dx);
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-            if (lane == 0) y[(int64_t)n * M + row] = acc;
-        }
-    } else {  // Q6_K x Q8_K, one super-block per lane step
-        const int64_t nb = K / 256;
-        for (int n = 0; n < N; ++n) {
-            float acc = 0.f;
-            for (int64_t b = lane; b < nb; b += 64) {
-                const uint8_t* wb = W + (row * nb + b) * kQ6_KBytes;
-                const uint8_t* xb = xq + ((int64_t)n * nb + b) * kQ8_KBytes;
-                int isum = 0;
-                for (int j = 0; j < 16; ++j) {
-                    const int sc = (int8_t)wb[192 + j];
-                    const int h = j >> 3, c = (j >> 1) & 3, kk = j & 1;
-                    int t = 0;
-                    for (int k4 = 0; k4 < 4; ++k4) {
-                        const int l = 16 * kk + 4 * k4;
-                        uint32_t qlw = ld_u16x2_g(wb + 64 * h + 32 * (c & 1) + l);
-                        const uint32_t lo = (c < 2) ? (qlw & 0x0F0F0F0Fu) : ((qlw >> 4) & 0x0F0F0F0Fu);
-                        const uint32_t hi = (ld_u16x2_g(wb + 128 + 32 * h + l) >> (2 * c)) & 0x03030303u;
-                        t = dot4(lo | (hi << 4), reinterpret_cast<const uint32_t*>(xb + 4)[4 * j + k4], t);
-                    }
-                    isum += sc * (t - 32 * (int)reinterpret_cast<const int16_t*>(xb + 260)[j]);
-                }
-                const float dw = h2f(reinterpret_cast<const uint16_t*>(wb + 208)[0]);
-                acc += (dw * reinterpret_cast<const float*>(xb)[0]) * (float)isum;
             }
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
@@ -888,7 +859,7 @@ hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const i
     GemvArgs a;
     a.nseg = nseg;
     a.G = (int)(K / 256);
-    a.GU = (int)(K / F::WPU);
+    a.GU = (int)(K / 256);
     a.rowB = (int64_t)a.GU * F::UB;
     const int Pl = a.GU >= 64 ? 64 : a.GU;
     int logP = 0;
@@ -937,14 +908,12 @@ hipError_t rowwave(int wtype, const void* W, const void* xq, float* y, int64_t M
     if (wtype == QMM_Q4_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q4_0>, g, b, 0, s, w, x, y, M, (int)N, K);
     else if (wtype == QMM_Q8_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q8_0>, g, b, 0, s, w, x, y, M, (int)N, K);
     else if (wtype == QMM_Q5_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q5_0>, g, b, 0, s, w, x, y, M, (int)N, K);
-    else if (wtype == QMM_Q6_K) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q6_K>, g, b, 0, s, w, x, y, M, (int)N, K);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 bool needs_rowwave(int wtype, int64_t K) {
-    if (wtype == QMM_Q6_K) return K % 2048 != 0;
-    return K % 256 != 0;
+    return wtype != QMM_Q6_K && K % 256 != 0;  // (Q6_K rows are whole 256-value super-blocks)
 }
 
 }  // namespace

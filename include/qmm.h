@@ -170,8 +170,8 @@ int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y,
  *                values, which the launch quantizes itself to the
  *                vec_dot_type with exactly the rule and results of
  *                qmm_quantize_act (the quantized rows are not written out)
- * The fp32 form needs N <= 8 and K a multiple of 256 (2048 for Q6_K);
- * otherwise it returns QMM_ERR_UNSUPPORTED.  Other errors as qmm_mul_mat. */
+ * The fp32 form needs N <= 8 and K a multiple of 256; otherwise it returns
+ * QMM_ERR_UNSUPPORTED.  Other errors as qmm_mul_mat. */
 int qmm_mul_mat_multi(int wtype, int count, const void* const* W, float* const* y, const int64_t* M,
                       const void* x, int x_is_f32, int64_t N, int64_t K, void* stream);
 

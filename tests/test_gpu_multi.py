@@ -31,7 +31,7 @@ def make_weights(g, wt, M, K):
 
 CASES = [(Q.QMM_Q4_0, 2048, (2048, 512, 512)), (Q.QMM_Q4_0, 8192, (2048,)), (Q.QMM_Q8_0, 2048, (300, 2048)),
          (Q.QMM_Q4_K, 4096, (4096, 1024, 1024)), (Q.QMM_Q4_K, 14336, (4096,)), (Q.QMM_Q6_K, 4096, (1000, 77)),
-         (Q.QMM_Q4_0, 256, (5, 3, 1, 9))]
+         (Q.QMM_Q6_K, 768, (33, 64)), (Q.QMM_Q6_K, 18176, (70,)), (Q.QMM_Q4_0, 256, (5, 3, 1, 9))]
 
 
 @pytest.mark.parametrize("wt,K,Ms", CASES)
@@ -66,5 +66,8 @@ def test_multi_errors():
     mm = Q.qmm_mul_mat_multi
     assert mm(Q.QMM_Q4_0, 1, [W], [y], [1], x, True, 9, 2048) == Q.QMM_ERR_UNSUPPORTED  # fp32 needs N <= 8
     assert mm(Q.QMM_Q4_0, 1, [W], [y], [1], x, True, 1, 96) == Q.QMM_ERR_UNSUPPORTED   # K % 256 != 0
-    assert mm(Q.QMM_Q6_K, 1, [W], [y], [1], x, True, 1, 256) == Q.QMM_ERR_UNSUPPORTED  # Q6_K: K % 2048 != 0
+    assert torch.all(y == 0).item()
+    # any whole number of Q6_K super-blocks is supported (zero weights: zero output)
+    assert mm(Q.QMM_Q6_K, 1, [W], [y], [1], x, True, 1, 256) == Q.QMM_OK
+    torch.cuda.synchronize()
     assert torch.all(y == 0).item()
