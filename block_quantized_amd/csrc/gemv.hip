@@ -21,8 +21,10 @@
 //    Q4_K, one 210 B super-block for Q6_K.  Consecutive lanes take
 //    consecutive units, so a wavefront reads one contiguous run of memory.
 //    Q6_K super-blocks are only 2-byte aligned: a lane reads 208 bytes from
-//    the 4-byte boundary at or below its super-block (13 loads) plus its last
-//    four bytes as two 2-byte loads, and shifts by the 0 or 2 byte skew.
+//    the 4-byte boundary at or below its super-block (14 loads of 16 bytes;
+//    the last unit of a matrix reads its own last 16 bytes instead of the
+//    14th, so nothing past the matrix is read), and shifts by the 0 or 2
+//    byte skew.
 //    (Measured on MI355X: per-lane 144 B units stream as fast as fully
 //    coalesced reads, ~6.3 TB/s, and so do the 210 B Q6_K units read this
 //    way; 8-super-block Q6_K units per lane, read in 224 B windows, streamed
@@ -43,8 +45,9 @@
 namespace qmm {
 namespace {
 
-// 16 bytes at a 4-byte-aligned address (Q6_K super-blocks are 2-byte aligned)
+// 16 bytes at a 4- or 2-byte-aligned address (Q6_K super-blocks are 2-byte aligned)
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 
 template <int WT> struct U;
 template <> struct U<QMM_Q4_0> { static constexpr int UB = 144, NV = 9; };
@@ -509,9 +512,10 @@ __device__ __forceinline__ void unit_q4_k(const uint32_t* w, const uint8_t* xr0,
 }
 
 // One Q6_K super-block.  r[0..51] are the 208 bytes from the 4-byte boundary
-// at or below its first byte, which is byte `skew` (0 or 2) of r; r[52] holds
-// its bytes 206-207 and r[53] its bytes 208-209 (d), each in the low half.
-// Dword i < 52 of the super-block is bytes skew + 4i .. of r.
+// at or below its first byte, which is byte `skew` (0 or 2) of r; when the
+// skew is 2, r[52] is its bytes 206-209 (unused when 0); r[53] holds d (its
+// bytes 208-209) in the low half.  Dword i < 52 of the super-block is bytes
+// skew + 4i .. of r.
 template <int NC>
 __device__ __forceinline__ void unit_q6_k(const uint32_t* r, uint32_t skew, const uint8_t* xr0, int xstride,
                                           float (&acc)[NC]) {
@@ -595,7 +599,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     // compiler's waits retire only the loads actually needed next.
     constexpr int kNoStore = 1 << 30;
     struct Loc {
-        const uint8_t* p;  // first byte of the unit (16-byte aligned); a dummy unit if !valid
+        const uint8_t* p;  // first byte of the unit; if !valid, the work item's first unit
         float* yb;         // output of the chunk's first row (wave-uniform)
         int64_t ldy;       // stride between output columns (the segment's M)
         int nrec;          // bytes of output rows of this chunk that exist (wave-uniform)
@@ -603,6 +607,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         int g;             // first 256-value activation group of the unit
         bool last;         // last chunk of its work item
         bool valid;
+        bool tail;         // the work item holds the last unit of its matrix (wave-uniform)
     };
     auto locate = [&](int64_t wi, int kc) {  // work item wi (uniform), chunk kc of it
         Loc L;
@@ -622,7 +627,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         const int64_t row = row0 + lr;
         const bool valid = gu < GU && lr < RW && row < M;
         L.valid = valid;
-        L.p = valid ? W + row * rowB + (int64_t)gu * F::UB : sW[0];
+        L.p = W + (valid ? row * rowB + (int64_t)gu * F::UB : row0 * rowB + (int64_t)kc * P * F::UB);
         L.yb = Y + row0;
         L.ldy = M;
         const int64_t left = M - row0;  // >= 1
@@ -630,22 +635,42 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         L.yoff = lwriter ? 4 * lr : kNoStore;
         L.g = gu;
         L.last = kc == NKC - 1;
+        L.tail = row0 + RW >= M && kc == NKC - 1;
         return L;
     };
-    // A unit's bytes: NV 16-byte pieces (Q6_K: 13 pieces from the 4-byte
-    // boundary at or below the unit, then its last 4 bytes as two halves, so
-    // no byte outside the unit's row is read).
+    // A unit's bytes: NV 16-byte pieces.  Q6_K: the 14 pieces from the 4-byte
+    // boundary at or below the unit, which end up to 14 bytes past it, in the
+    // next unit.  The work item that holds the last unit of a matrix (a
+    // wave-uniform choice, so no load sits behind a lane-level branch) takes
+    // the unit's own last 16 bytes as the 14th piece instead, so no byte past
+    // the matrix is read.  Either way dword 52 becomes the unit's bytes
+    // 206-209 when the skew is 2, and dword 53 holds d (bytes 208-209) in its
+    // low half.
     auto load = [&](const Loc& L, uint4 (&v)[NV]) {
         if constexpr (WT == QMM_Q6_K) {
-            const u32x4_a4* q = reinterpret_cast<const u32x4_a4*>(
-                reinterpret_cast<uintptr_t>(L.p) & ~static_cast<uintptr_t>(3));
+            // (pointer arithmetic, not an integer round trip: the compiler
+            // then still knows the address is global memory and emits
+            // global loads, not flat ones, which would also count against
+            // the LDS wait counter)
+            const u32x4_a4* q = reinterpret_cast<const u32x4_a4*>(L.p - (reinterpret_cast<uintptr_t>(L.p) & 3u));
 #pragma unroll
             for (int i = 0; i < NV - 1; ++i) {
                 const u32x4_a4 t = q[i];
                 v[i] = make_uint4(t.x, t.y, t.z, t.w);
             }
-            const uint16_t* h = reinterpret_cast<const uint16_t*>(L.p);
-            v[NV - 1] = make_uint4(h[103], h[104], 0u, 0u);
+            // (This form makes the compiler wait for the prefetch before the
+            // unit is computed, so a wave does not overlap its own loads with
+            // its compute.  Measured on the 128256x4096 head, it is 5-8%
+            // faster than the forms whose waits let the loads run under the
+            // compute: 83-85 us against 87-92 us.)
+            if (L.tail) {
+                const u32x4_a2 t = *reinterpret_cast<const u32x4_a2*>(L.p + (kQ6_KBytes - 16));
+                v[NV - 1] = make_uint4(t.w, t.w >> 16, 0u, 0u);
+            } else {
+                const u32x4_a4 t = q[NV - 1];
+                const uint32_t sk = (uint32_t)reinterpret_cast<uintptr_t>(L.p) & 3u;
+                v[NV - 1] = make_uint4(t.x, t.x >> (8 * sk), 0u, 0u);
+            }
         } else {
             const uint4* q = reinterpret_cast<const uint4*>(L.p);
 #pragma unroll
