@@ -20,15 +20,16 @@
 //    (144 B) for Q4_0, 8 blocks (272 B) for Q8_0, one 144 B super-block for
 //    Q4_K, one 210 B super-block for Q6_K.  Consecutive lanes take
 //    consecutive units, so a wavefront reads one contiguous run of memory.
-//    Q6_K super-blocks are only 2-byte aligned: a lane reads 208 bytes from
+//    Q6_K super-blocks are only 2-byte aligned: a lane reads 224 bytes from
 //    the 4-byte boundary at or below its super-block (14 loads of 16 bytes;
-//    the last unit of a matrix reads its own last 16 bytes instead of the
-//    14th, so nothing past the matrix is read), and shifts by the 0 or 2
-//    byte skew.
+//    the work item holding a matrix's last unit reads each unit's own last
+//    16 bytes instead of the 14th piece, so nothing past the matrix is
+//    read), and shifts by the 0 or 2 byte skew.
 //    (Measured on MI355X: per-lane 144 B units stream as fast as fully
 //    coalesced reads, ~6.3 TB/s, and so do the 210 B Q6_K units read this
-//    way; 8-super-block Q6_K units per lane, read in 224 B windows, streamed
-//    at 2.4 TB/s in the same probe.  Staging through LDS halved the rate.)
+//    way; 8-super-block Q6_K units per lane, read in 224 B windows 1680 B
+//    apart, streamed at 2.4 TB/s in the same probe.  Staging through LDS
+//    halved the rate.)
 //  * Loads run one step ahead (two register buffers), and the first step's
 //    loads are issued before the activations are staged.
 //  * A row of K weights is GU units; P = next power of two >= min(GU, 64)
