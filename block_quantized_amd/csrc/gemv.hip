@@ -32,9 +32,9 @@
 //    halved the rate.)
 //  * Loads run one step ahead (two register buffers), and the first step's
 //    loads are issued before the activations are staged.
-//  * A row of K weights is GU units; P = next power of two >= min(GU, 64)
+//  * A row of K weights is G = K/256 units; P = next power of two >= min(G, 64)
 //    lanes share a row, a wavefront covers RW = 64/P rows per chunk, or a
-//    row in ceil(GU/64) chunks when GU > 64.  Lanes of a row are reduced with
+//    row in ceil(G/64) chunks when G > 64.  Lanes of a row are reduced with
 //    a fixed butterfly, so results are bit-identical run to run.
 //  * Several matrices sharing K and x (e.g. q|k|v, gate|up) can form one
 //    launch: their chunks are concatenated ("segments").
@@ -76,8 +76,7 @@ struct GemvArgs {
     const uint8_t* xq;
     int64_t rowB;      // bytes per W row
     int64_t nwork;     // work items over all segments
-    int G;             // 256-value activation groups per row (K / 256)
-    int GU;            // lane units per row
+    int G;             // 256-value groups per row (K / 256): activation records and lane units
     int logP;          // log2(lanes per row)
     int RW;            // rows per chunk
     int nkc;           // chunks per work item
@@ -565,7 +564,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
 
     // Every argument is read once, up front, so the kernel-argument loads form
     // one batch (no dependent scalar round trips before the first W load).
-    const int nseg = a.nseg, GU = a.GU, logP = a.logP, RW = a.RW, NKC = a.nkc;
+    const int nseg = a.nseg, logP = a.logP, RW = a.RW, NKC = a.nkc;
     const int64_t rowB = a.rowB, nwork = a.nwork;
     const uint8_t* xq = a.xq;
     const int G = a.G;
@@ -626,7 +625,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         const int64_t row0 = (wi - w0) * RW;  // uniform
         const int gu = kc * P + lg;  // kc is 0 when a row fits one chunk
         const int64_t row = row0 + lr;
-        const bool valid = gu < GU && lr < RW && row < M;
+        const bool valid = gu < G && lr < RW && row < M;
         L.valid = valid;
         L.p = W + (valid ? row * rowB + (int64_t)gu * F::UB : row0 * rowB + (int64_t)kc * P * F::UB);
         L.yb = Y + row0;
@@ -885,14 +884,13 @@ hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const i
     GemvArgs a;
     a.nseg = nseg;
     a.G = (int)(K / 256);
-    a.GU = (int)(K / 256);
-    a.rowB = (int64_t)a.GU * F::UB;
-    const int Pl = a.GU >= 64 ? 64 : a.GU;
+    a.rowB = (int64_t)a.G * F::UB;
+    const int Pl = a.G >= 64 ? 64 : a.G;
     int logP = 0;
     while ((1 << logP) < Pl) ++logP;
     a.logP = logP;
     a.RW = 64 >> logP;
-    a.nkc = (a.GU + (1 << logP) - 1) >> logP;
+    a.nkc = (a.G + (1 << logP) - 1) >> logP;
     int64_t work = 0;
     for (int i = 0; i < nseg; ++i) {
         a.seg[i].W = static_cast<const uint8_t*>(Ws[i]);
