@@ -43,6 +43,8 @@
 //    int8 codes, then the fp32 scales and precomputed integer sums.
 #include "qmm_internal.h"
 
+#include <atomic>
+
 namespace qmm {
 namespace {
 
@@ -841,19 +843,25 @@ DevInfo& dev_info() {
 
 template <int WT, int NC, bool XF>
 hipError_t launch_one(const GemvArgs& a, size_t lds, int wpg, hipStream_t s) {
-    static int occ[9] = {0};  // workgroups per CU, by waves per workgroup
-    if (!occ[wpg]) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<WT, NC, XF>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    // Workgroups per CU as registers and waves allow, by waves per workgroup
+    // (LDS, which depends on K and the column count, is applied below).
+    // Written once per entry; concurrent first calls store the same value.
+    static std::atomic<int> occ[9];
+    int occw = occ[wpg].load(std::memory_order_relaxed);
+    if (!occw) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<WT, NC, XF>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<WT, NC, XF>, wpg * 64, lds) !=
-                hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<WT, NC, XF>, wpg * 64, 0) != hipSuccess ||
             n <= 0)
             n = 1;
-        occ[wpg] = n;
+        occw = n;
+        occ[wpg].store(n, std::memory_order_relaxed);
     }
     const DevInfo& di = dev_info();
-    const int per_cu = (int)(di.lds / (lds ? lds : 1)) < occ[wpg] ? (int)(di.lds / (lds ? lds : 1)) : occ[wpg];
+    const int by_lds = (int)(di.lds / (lds ? lds : 1));
+    const int per_cu = by_lds < occw ? by_lds : occw;
     const int64_t need = (a.nwork + wpg - 1) / wpg;
     const int64_t cap = (int64_t)di.cus * (per_cu > 0 ? per_cu : 1);
     const int grid = (int)(need < cap ? need : cap);
