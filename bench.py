@@ -428,11 +428,10 @@ def traffic_summary(fetch_csv, write_csv):
     print("# HBM traffic: fused Q4_0 GEMV (decode sweep, 1B-Llama shapes, batch 1)\n")
     print("Counter runs (from the repository root on one MI355X, each a run of its own):\n")
     print("```")
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        print(f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c.split('_')[0].lower()} -o run --output-format csv "
+    for c, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        print(f"rocprofv3 --pmc {c} -d {os.path.dirname(path)} -o run --output-format csv "
               "-- python -u bench.py --quick --no-cpu --steps 2 --warmup 1")
-    print("python bench.py --traffic gpurun_out/pmc_fetch/run_counter_collection.csv "
-          "gpurun_out/pmc_write/run_counter_collection.csv")
+    print(f"python bench.py --traffic {fetch_csv} {write_csv}")
     print("```\n")
     print("| counter | 256 MiB copy, counter (KiB) | scale factor | head dispatches | head avg (KiB) | bytes per launch |")
     print("|---|---|---|---|---|---|")
