@@ -295,54 +295,103 @@ def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=
             "tops": 2 * M * N * K * launches / sec / 1e12, "copies": copies}
 
 
-def kv_cache_workloads(b: Bench, reps=20):
+def rotating_workload(b: Bench, launch, copies, bytes_per_launch, min_launches=8, reps=4):
+    """Per-launch time of launch(i) (i = copy index), in a graph that cycles
+    through `copies` buffer sets, so that no launch finds its data in the
+    256 MB Infinity Cache, with at least `min_launches` launches per graph."""
+    torch = b.torch
+    n = max(min_launches, copies)
+
+    def run():
+        for k in range(n):
+            launch(k % copies)
+    sec = b.time_graph(b.graph(run), reps, 2)
+    return {"us_per_launch": sec / (reps * n) * 1e6, "bytes_per_launch": bytes_per_launch,
+            "gbs": bytes_per_launch * reps * n / sec / 1e9, "frac_hbm": bytes_per_launch * reps * n / sec / 1e9 / HBM_PEAK_GBS,
+            "copies": copies}
+
+
+def kv_cache_workloads(b: Bench, want):
     """Q8_0 KV cache of the 8B GQA model (1024 values per token and layer for
     K and for V): quantizing a 512-token prompt for all 32 layers (one slab),
     appending one decode token (K and V rows of one layer: a 2-row launch),
-    and reading a 32768-token cache of one layer back to fp32."""
+    and reading a 32768-token cache of one layer back to fp32.  The slab
+    launches rotate over three buffer sets (507 MB), so each reads HBM."""
     import synth
     torch, Q = b.torch, b.Q
     row = synth.LLAMA_8B_KV_ROW
     rowb = Q.qmm_row_bytes(Q.QMM_Q8_0, row)
     g = synth.rng(0)
     out = {}
+    lib = Q.lib()
+    st = lambda: torch.cuda.current_stream().cuda_stream
     # prefill: 2 x 32 layers x 512 tokens = 32768 rows
     rows = 2 * synth.LLAMA_8B_KV["layers"] * 512
-    x = torch.from_numpy(synth.normal_f32(g, (rows, row), 1.0)).to(b.dev)
-    cache = torch.empty((rows, rowb), dtype=torch.uint8, device=b.dev)
-    lib = Q.lib()
-
-    def quant():
-        lib.qmm_quantize_act(Q.QMM_Q8_0, x.data_ptr(), cache.data_ptr(), rows, row,
-                             torch.cuda.current_stream().cuda_stream)
-    sec = b.time_graph(b.graph(quant), reps, 2)
-    by = rows * row * 4 + rows * rowb
-    out["kv_q8_0_prefill_quantize_32768x1024"] = {"us_per_launch": sec / reps * 1e6, "bytes_per_launch": by,
-                                                  "gbs": by * reps / sec / 1e9}
+    x0 = torch.from_numpy(synth.normal_f32(g, (rows, row), 1.0)).to(b.dev)
+    xs = [x0] + [x0.clone() for _ in range(2)]
+    caches = [torch.empty((rows, rowb), dtype=torch.uint8, device=b.dev) for _ in range(3)]
+    if want("kv_q8_0_prefill_quantize_32768x1024"):
+        out["kv_q8_0_prefill_quantize_32768x1024"] = rotating_workload(
+            b, lambda i: lib.qmm_quantize_act(Q.QMM_Q8_0, xs[i].data_ptr(), caches[i].data_ptr(), rows, row, st()),
+            3, rows * row * 4 + rows * rowb)
+    for i in range(3):  # the caches hold real codes for the read-back below
+        lib.qmm_quantize_act(Q.QMM_Q8_0, xs[i].data_ptr(), caches[i].data_ptr(), rows, row, st())
     # decode append: one token's K and V rows for each of the 32 layers, one
     # 2-row launch per layer (32 launches in the graph)
     L = synth.LLAMA_8B_KV["layers"]
+    if want("kv_q8_0_decode_append_2x1024"):
+        def append():
+            for layer in range(L):
+                lib.qmm_quantize_act(Q.QMM_Q8_0, xs[0].data_ptr() + 2 * layer * row * 4,
+                                     caches[0].data_ptr() + (2 * layer * 512 + 7) * rowb, 2, row, st())
+        reps = 20
+        sec = b.time_graph(b.graph(append), reps, 2)
+        out["kv_q8_0_decode_append_2x1024"] = {"us_per_launch": sec / (reps * L) * 1e6,
+                                               "bytes_per_launch": 2 * (row * 4 + rowb), "launches_per_token": L}
+    # read back a 32768-token cache to fp32 (into the x buffers, no longer needed)
+    if want("kv_q8_0_dequantize_32768x1024"):
+        out["kv_q8_0_dequantize_32768x1024"] = rotating_workload(
+            b, lambda i: lib.qmm_dequantize(Q.QMM_Q8_0, caches[i].data_ptr(), xs[i].data_ptr(), rows, row, st()),
+            3, rows * rowb + rows * row * 4)
+    del xs, caches, x0
+    torch.cuda.empty_cache()
+    return out
 
-    def append():
-        st = torch.cuda.current_stream().cuda_stream
-        for layer in range(L):
-            lib.qmm_quantize_act(Q.QMM_Q8_0, x.data_ptr() + 2 * layer * row * 4,
-                                 cache.data_ptr() + (2 * layer * 512 + 7) * rowb, 2, row, st)
-    sec = b.time_graph(b.graph(append), reps, 2)
-    by = 2 * (row * 4 + rowb)
-    out["kv_q8_0_decode_append_2x1024"] = {"us_per_launch": sec / (reps * L) * 1e6, "bytes_per_launch": by,
-                                           "launches_per_token": L}
-    # read back one layer's 32768-token K cache
-    deq = torch.empty((rows, row), dtype=torch.float32, device=b.dev)
 
-    def dequant():
-        lib.qmm_dequantize(Q.QMM_Q8_0, cache.data_ptr(), deq.data_ptr(), rows, row,
-                           torch.cuda.current_stream().cuda_stream)
-    sec = b.time_graph(b.graph(dequant), reps, 2)
-    by = rows * rowb + rows * row * 4
-    out["kv_q8_0_dequantize_32768x1024"] = {"us_per_launch": sec / reps * 1e6, "bytes_per_launch": by,
-                                            "gbs": by * reps / sec / 1e9}
-    del x, cache, deq
+def codec_workloads(b: Bench, want):
+    """Activation quantization for the batch-512 prefill (fp32 512 x 4096 to
+    Q8_K), and dequantization of 14336 x 4096 Q4_K and Q6_K weights to fp32,
+    rotating over enough buffer sets to exceed the Infinity Cache."""
+    import synth
+    torch, Q = b.torch, b.Q
+    lib = Q.lib()
+    st = lambda: torch.cuda.current_stream().cuda_stream
+    g = synth.rng(0)
+    out = {}
+    if want("q8_k_quantize_512x4096"):
+        N, K = 512, 4096
+        rb = Q.qmm_row_bytes(Q.QMM_Q8_K, K)
+        x0 = torch.from_numpy(synth.normal_f32(g, (N, K), 1.0)).to(b.dev)
+        c = 32  # 32 x 10.8 MB
+        xs = [x0] + [x0.clone() for _ in range(c - 1)]
+        qs = [torch.empty((N, rb), dtype=torch.uint8, device=b.dev) for _ in range(c)]
+        out["q8_k_quantize_512x4096"] = rotating_workload(
+            b, lambda i: lib.qmm_quantize_act(Q.QMM_Q8_K, xs[i].data_ptr(), qs[i].data_ptr(), N, K, st()),
+            c, N * K * 4 + N * rb)
+        del xs, qs, x0
+    for name, wt, make in (("q4_k", Q.QMM_Q4_K, synth.q4_k_random), ("q6_k", Q.QMM_Q6_K, synth.q6_k_random)):
+        key = f"{name}_dequantize_14336x4096"
+        if not want(key):
+            continue
+        M, K = 14336, 4096
+        W0 = b.gpu_u8(make(g, M, K))
+        c = 2  # 2 x (33-48 MB in + 235 MB out)
+        Ws = [W0] + [W0.clone() for _ in range(c - 1)]
+        ys = [torch.empty((M, K), dtype=torch.float32, device=b.dev) for _ in range(c)]
+        out[key] = rotating_workload(
+            b, lambda i: lib.qmm_dequantize(wt, Ws[i].data_ptr(), ys[i].data_ptr(), M, K, st()),
+            c, W0.numel() + M * K * 4)
+        del Ws, ys, W0
     torch.cuda.empty_cache()
     return out
 
@@ -382,9 +431,13 @@ def secondary(b: Bench, only=None):
             r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
             out[f"{name}_gemm_4096x4096_b512"] = r
             progress(f"{name} gemm 4096x4096 b512 {r['tops']:.1f} TOPS")
-    if want("kv_q8_0"):
-        out.update(kv_cache_workloads(b))
+    if any(want(k) for k in ("kv_q8_0_prefill_quantize_32768x1024", "kv_q8_0_decode_append_2x1024",
+                             "kv_q8_0_dequantize_32768x1024")):
+        out.update(kv_cache_workloads(b, want))
         progress("kv cache q8_0 done")
+    if any(want(k) for k in ("q8_k_quantize_512x4096", "q4_k_dequantize_14336x4096", "q6_k_dequantize_14336x4096")):
+        out.update(codec_workloads(b, want))
+        progress("codecs done")
     return out
 
 

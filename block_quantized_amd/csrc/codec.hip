@@ -193,14 +193,16 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t* __rest
 // bytes 0-3 / 4-7, the low nibbles of sc4-7 / m4-7 in the low / high nibbles
 // of bytes 8-11, and bits 4-5 of sc4-7 / m4-7 in the top two bits of bytes
 // 0-3 / 4-7.
-__device__ __forceinline__ void q4k_scale_min(const uint8_t* s, int j, int& sc, int& m) {
-    if (j < 4) {
-        sc = s[j] & 63;
-        m = s[j + 4] & 63;
-    } else {
-        sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
-        m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
-    }
+// (The 16-byte header d, dmin, scales is read as one 16-byte load, which
+// every lane of a super-block shares, and both forms are computed and one
+// selected: with byte loads behind a branch on j, half the lanes waited for
+// a second memory round trip.)
+__device__ __forceinline__ void q4k_scale_min(const uint4& hdr, int j, int& sc, int& m) {
+    const int sh = 8 * (j & 3);
+    const uint32_t s0 = (hdr.y >> sh) & 0xFF, s1 = (hdr.z >> sh) & 0xFF, s2 = (hdr.w >> sh) & 0xFF;
+    const bool lo = j < 4;
+    sc = (int)(lo ? (s0 & 63) : ((s2 & 15) | ((s0 >> 6) << 4)));
+    m = (int)(lo ? (s1 & 63) : ((s2 >> 4) | ((s1 >> 6) << 4)));
 }
 
 __global__ __launch_bounds__(256) void dequant_q4_k_kernel(const uint8_t* __restrict__ w, float* __restrict__ out,
@@ -210,12 +212,12 @@ __global__ __launch_bounds__(256) void dequant_q4_k_kernel(const uint8_t* __rest
     const int64_t b = t >> 6;
     const int l = (int)(t & 63);
     const uint8_t* blk = w + b * kQ4_KBytes;
-    const uint32_t dd = reinterpret_cast<const uint32_t*>(blk)[0];
-    const float d = h2f(dd), dmin = h2f(dd >> 16);
     const int j = l >> 3;
-    int sc, m;
-    q4k_scale_min(blk + 4, j, sc, m);
     uint32_t qs = reinterpret_cast<const uint32_t*>(blk + 16 + 32 * (j >> 1))[l & 7];
+    const uint4 hdr = reinterpret_cast<const uint4*>(blk)[0];
+    const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
+    int sc, m;
+    q4k_scale_min(hdr, j, sc, m);
     if (j & 1) qs >>= 4;
     const float a = d * (float)sc;
     const float c = dmin * (float)m;
