@@ -141,3 +141,14 @@ def test_codecs_deterministic():
     W = to_gpu(synth.q6_k_random(g, 128, 4096))
     d = [to_cpu(Q.dequantize(Q.QMM_Q6_K, W, 128, 4096)) for _ in range(3)]
     assert all(np.array_equal(d[0].view(np.uint32), b.view(np.uint32)) for b in d[1:])
+
+
+@pytest.mark.parametrize("t", [Q.QMM_Q4_K, Q.QMM_Q6_K])
+def test_dequantize_bench_size(t):
+    # the 14336 x 4096 dequantization the benchmark times, every value bit-exact
+    g = synth.rng(0)
+    W = (synth.q4_k_random if t == Q.QMM_Q4_K else synth.q6_k_random)(g, 14336, 4096)
+    say("dequant bench size", t)
+    ot = O.Q4_K if t == Q.QMM_Q4_K else O.Q6_K
+    assert_f32_bits_equal(to_cpu(Q.dequantize(t, to_gpu(W), 14336, 4096)), O.dequantize(ot, W, 14336, 4096),
+                          f"type {t} 14336x4096")

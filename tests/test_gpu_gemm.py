@@ -239,3 +239,19 @@ def test_gemm_q32_extremes_and_determinism(wtype):
     y_ref, T = O.mul_mat(ow, W, xq, M, N, K)
     assert_within_tolerance(outs[0], y_ref, T, what="q32 extremes")
     assert np.all(outs[0][3] == 0)
+
+
+@pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
+def test_gemm_q32_bench_size_sampled(wtype):
+    # the 4096 x 4096, N = 512 product the benchmark times (automatic choice),
+    # checked on sampled weight rows against the oracle
+    M, N, K = 4096, 512, 4096
+    g = synth.rng(0)
+    W = _q32_weights(g, wtype, M, K)
+    xq = O.quantize(O.Q8_0, synth.normal_f32(g, (N, K), 1.0))
+    print("gemm q32 bench size", wtype, flush=True)
+    y = to_cpu(Q.mul_mat(wtype, to_gpu(W), to_gpu(xq), M, N, K))
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], g.integers(0, M, 40)]))
+    ow = {Q.QMM_Q4_0: O.Q4_0, Q.QMM_Q5_0: O.Q5_0, Q.QMM_Q8_0: O.Q8_0}[wtype]
+    y_ref, T = O.mul_mat(ow, np.ascontiguousarray(W[rows]), xq, len(rows), N, K)
+    assert_within_tolerance(y[:, rows], y_ref, T, what=f"GEMM type {wtype} 4096x4096 N=512")
