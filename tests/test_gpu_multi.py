@@ -29,7 +29,9 @@ def make_weights(g, wt, M, K):
     return O.quantize(O.Q8_0 if wt == Q.QMM_Q8_0 else O.Q4_0, synth.normal_f32(g, (M, K), 0.02))
 
 
-CASES = [(Q.QMM_Q4_0, 2048, (2048, 512, 512)), (Q.QMM_Q4_0, 8192, (2048,)), (Q.QMM_Q8_0, 2048, (300, 2048)),
+# the first four are the launches of the 1B-Llama decode sweep (q|k|v, ffn_down, o, gate|up)
+CASES = [(Q.QMM_Q4_0, 2048, (2048, 512, 512)), (Q.QMM_Q4_0, 8192, (2048,)), (Q.QMM_Q4_0, 2048, (2048,)),
+         (Q.QMM_Q4_0, 2048, (8192, 8192)), (Q.QMM_Q8_0, 2048, (300, 2048)),
          (Q.QMM_Q4_K, 4096, (4096, 1024, 1024)), (Q.QMM_Q4_K, 14336, (4096,)), (Q.QMM_Q6_K, 4096, (1000, 77)),
          (Q.QMM_Q6_K, 768, (33, 64)), (Q.QMM_Q6_K, 18176, (70,)), (Q.QMM_Q4_0, 256, (5, 3, 1, 9))]
 
