@@ -89,7 +89,6 @@ __device__ __forceinline__ bool xcd_tile(int nb, int total, int& rb, int& cb) {
 }
 
 constexpr int kCodeStride = 272;  // LDS bytes per activation row's 256 codes (+16: bank spread)
-constexpr int kSumStride = 32;    // LDS bytes per activation row's 16 sums as fp16
 
 // bytes b of v (4 quants <= 15) times s (<= 7): each product <= 105 stays in its byte
 __device__ __forceinline__ uint32_t mul_bytes(uint32_t v, uint32_t s) {
@@ -126,18 +125,35 @@ struct XTile {
 // that reading one tile never waits for the copy into the other; the
 // barrier that ends each super-block waits for the copy.  The buffer descriptor covers only this workgroup's
 // activation rows: rows past N read as zeros (their outputs are not stored).
-template <int NT>
-__global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
+//
+// KS = 2 splits K between two groups of 4 waves (the first and second half
+// of the super-blocks, each with its own pair of tiles); the second group
+// hands its partial sums to the first through LDS at the end, which adds
+// them in a fixed order.  It doubles the waves of a grid that has no more
+// workgroups than the GPU has CUs.
+template <int BN, int KS>
+struct XTiles {
+    XTile<BN> h[KS];
+};
+
+template <int NT, int KS>
+__global__ __launch_bounds__(256 * KS, 2 / KS) void gemm_q4k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
                                                        float* __restrict__ Y, int M, int N, int SB,
                                                        int mblk, int nblk) {
     constexpr int BN = NT * 32;  // activation rows per workgroup
     static_assert(BN % 32 == 0 && BN <= 64, "staging assumes 4 waves and at most 64 rows");
-    __shared__ __attribute__((aligned(16))) XTile<BN> tile0;
-    __shared__ __attribute__((aligned(16))) XTile<BN> tile1;
+    static_assert(KS == 1 || KS == 2, "K is split in at most two");
+    __shared__ __attribute__((aligned(16))) XTiles<BN, KS> tiles0;
+    __shared__ __attribute__((aligned(16))) XTiles<BN, KS> tiles1;
 
     // wave-uniform (scalar) wave index: the copies' LDS addresses go to M0
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x, lane = tid & 63, wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wave_all & 3, kh = wave_all >> 2;  // row wave, K part
     const int c = lane & 31, h = lane >> 5;
+    XTile<BN>& tile0 = tiles0.h[kh];
+    XTile<BN>& tile1 = tiles1.h[kh];
+    // this K part's super-blocks (the launcher makes SB a multiple of KS)
+    const int sb0 = kh * (SB / KS), sb1 = sb0 + SB / KS;
     int rb, cb;
     if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
     const int m0 = rb * 128 + wave * 32;
@@ -175,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
     // super-block of compute does not cover a load from HBM
     uint4 wh, wq[4], wh2, wq2[4];
     auto w_load = [&](int sb, uint4& hdr, uint4 (&q)[4]) {
-        sb = min(sb, SB - 1);  // past the end: a harmless repeat of the last super-block
+        sb = min(sb, sb1 - 1);  // past the end: a harmless repeat of the last super-block
         const uint8_t* b = wrow + (int64_t)sb * kQ4_KBytes;
         hdr = reinterpret_cast<const uint4*>(b)[0];
 #pragma unroll
@@ -200,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
         // the activation copy goes first: loads retire in order, and the
         // barrier that ends this super-block waits for the copy but not for
         // the weights of super-block sb + 2 issued after it
-        if (sb + 1 < SB) x_copy(Tn, sb + 1);
+        if (sb + 1 < sb1) x_copy(Tn, sb + 1);
         w_load(sb + 2, wh2, wq2);
         const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
         const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
@@ -263,15 +279,34 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const uint8_t* __restr
         __syncthreads();  // the next tile has landed (waits for the copies) and this one is free
     };
 
-    w_load(0, wh, wq);
-    x_copy(tile0, 0);
-    w_load(1, wh2, wq2);
+    w_load(sb0, wh, wq);
+    x_copy(tile0, sb0);
+    w_load(sb0 + 1, wh2, wq2);
     __syncthreads();
     // (each arm names its tiles statically, which is what lets the compiler
     // tell the two apart)
-    for (int sb = 0; sb < SB; ++sb) {
-        if (sb & 1) step(sb, tile1, tile0);
-        else step(sb, tile0, tile1);
+    for (int i = 0; i < SB / KS; ++i) {
+        if (i & 1) step(sb0 + i, tile1, tile0);
+        else step(sb0 + i, tile0, tile1);
+    }
+
+    if constexpr (KS == 2) {
+        // the second K part's sums, through LDS (the tiles are free: the
+        // last step issued no copy and ended with a barrier)
+        static_assert(sizeof(XTiles<BN, KS>) >= 4 * NT * 16 * 64 * sizeof(float), "partials fit a tile pair");
+        float* red = reinterpret_cast<float*>(&tiles0);
+        if (kh == 1) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[((wave * NT + t) * 16 + r) * 64 + lane] = yacc[t][r];
+        }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yacc[t][r] += red[((wave * NT + t) * 16 + r) * 64 + lane];
     }
 
     const int m = m0 + c;
@@ -898,6 +933,9 @@ bool gemm_supported(int wtype) {
     return wtype == QMM_Q4_K || wtype == QMM_Q6_K || wtype == QMM_Q4_0 || wtype == QMM_Q5_0 || wtype == QMM_Q8_0;
 }
 
+// Grids up to this many Q4_K tiles (one per CU) split K in two
+constexpr int64_t kSplitKMaxTiles = 256;
+
 hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
     if (!gemm_supported(wtype)) return hipErrorNotSupported;
@@ -960,8 +998,12 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
     // 64 activation rows per workgroup: two waves per SIMD fit (the 128-row
     // tile needs one SIMD's registers per wave), measured faster at every size
     const int64_t nb = (N + 63) / 64;
-    hipLaunchKernelGGL(gemm_q4k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
-                       (int)mblocks, (int)nb);
+    if (mblocks * nb <= kSplitKMaxTiles && SB % 2 == 0)  // K split in two: 8 waves per workgroup
+        hipLaunchKernelGGL((gemm_q4k_kernel<2, 2>), grid(mblocks * nb), dim3(512), 0, s, w, x, y, (int)M, (int)N,
+                           SB, (int)mblocks, (int)nb);
+    else
+        hipLaunchKernelGGL((gemm_q4k_kernel<2, 1>), grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N,
+                           SB, (int)mblocks, (int)nb);
     return hipGetLastError();
 }
 

@@ -4,8 +4,9 @@ The product of page 'The GGML ecosystem, and where synapse fits', section 5
 ('Products: weights against quantized activations'), on matrix cores: every
 output must satisfy |y - y_ref| <= 1e-5 * T against the CPU oracle, for
 ragged M and N (partial tiles in both directions), both workgroup tile
-widths, and any N through algo=2; results are deterministic and nothing is
-written past y."""
+widths, grids with K split between two wave groups (at most 256 tiles and an
+even count of super-blocks) and without, and any N through algo=2; results
+are deterministic and nothing is written past y."""
 import numpy as np
 import pytest
 import torch
@@ -23,7 +24,8 @@ def run(W, xq, M, N, K, algo=2):
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 256), (1, 9, 256), (31, 33, 512), (130, 100, 768), (300, 129, 1024),
-                                   (128, 512, 4096), (4113, 64, 2048), (77, 1, 256), (64, 8, 512), (2000, 200, 256)])
+                                   (128, 512, 4096), (4113, 64, 2048), (77, 1, 256), (64, 8, 512), (2000, 200, 256),
+                                   (16384, 65, 512), (16400, 65, 512)])
 def test_gemm_q4k_shapes(M, N, K):
     g = np.random.default_rng(M * 7 + N * 13 + K)
     W = synth.q4_k_random(g, M, K)
