@@ -562,17 +562,27 @@ struct Q32W<QMM_Q5_0> {
     }
 };
 
-template <int WT>
-__global__ __launch_bounds__(256, 2) void gemm_q32_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int N, int NB,
-                                                       int mblk, int nblk) {
+// KS = 2 or 4 splits the chunks between KS groups of 4 waves, as in the Q4_K
+// kernel (the launcher takes it only when the chunks are full and their
+// count is a multiple of KS).  The partial sums are added through LDS in a
+// fixed tree, (p0 + p2) + (p1 + p3) for four parts, so results are
+// deterministic.
+template <int WT, int KS>
+__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(const uint8_t* __restrict__ W,
+                                                                 const uint8_t* __restrict__ X,
+                                                                 float* __restrict__ Y, int M, int N, int NB,
+                                                                 int mblk, int nblk) {
     constexpr int BN = 64, CB = 4;          // activation rows per workgroup, blocks per chunk
     constexpr int CS = 32 * CB + 16;        // LDS row stride of a chunk's codes
-    __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][CS];
-    __shared__ __attribute__((aligned(16))) float s_dx[2][CB][BN];
+    static_assert(KS == 1 || KS == 2 || KS == 4, "K is split in 1, 2 or 4 parts");
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes_all[KS][2][BN][CS];
+    __shared__ __attribute__((aligned(16))) float s_dx_all[KS][2][CB][BN];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+    const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);  // K part
     const int c = lane & 31, h = lane >> 5;
+    auto& s_codes = s_codes_all[kh];
+    auto& s_dx = s_dx_all[kh];
     int rb, cb;
     if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
     const int m0 = rb * 128 + wave * 32;
@@ -611,17 +621,18 @@ __global__ __launch_bounds__(256, 2) void gemm_q32_kernel(const uint8_t* __restr
 #pragma unroll
         for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
 
-    const int nchunks = nch + (tail ? 1 : 0);
-    x_load(0);
-    w_load(0);
+    // this K part's chunks
+    const int nper = (nch + (tail ? 1 : 0)) / KS, ch0 = kh * nper;
+    x_load(ch0);
+    w_load(ch0);
     x_store(0);
     __syncthreads();
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int buf = ch & 1;
+    for (int i = 0; i < nper; ++i) {
+        const int ch = ch0 + i, buf = i & 1;
         Q32W<WT> w[CB];
 #pragma unroll
         for (int j = 0; j < CB; ++j) w[j] = wn[j];
-        if (ch + 1 < nchunks) {
+        if (i + 1 < nper) {
             x_load(ch + 1);
             w_load(ch + 1);
         }
@@ -645,8 +656,37 @@ __global__ __launch_bounds__(256, 2) void gemm_q32_kernel(const uint8_t* __restr
                 }
             }
         }
-        if (ch + 1 < nchunks) x_store(buf ^ 1);
+        if (i + 1 < nper) x_store(buf ^ 1);
         __syncthreads();
+    }
+
+    if constexpr (KS > 1) {
+        // the tiles are free: the last chunk ended with a barrier.  Level s:
+        // parts s .. 2s-1 hand their sums to parts 0 .. s-1.  Every wave
+        // takes every barrier; only part 0 goes on to the stores.
+        constexpr int kPart = 4 * 2 * 16 * 64;  // floats of one part's sums
+        static_assert(sizeof(s_codes_all) >= KS / 2 * kPart * sizeof(float), "partials fit the code tiles");
+        float* red = reinterpret_cast<float*>(&s_codes_all[0][0][0][0]);
+#pragma unroll
+        for (int lv = KS / 2; lv >= 1; lv /= 2) {
+            if (kh >= lv && kh < 2 * lv) {
+                float* dst = red + (kh - lv) * kPart;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[((wave * 2 + t) * 16 + r) * 64 + lane] = yacc[t][r];
+            }
+            __syncthreads();
+            if (kh < lv) {
+                const float* src = red + kh * kPart;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) yacc[t][r] += src[((wave * 2 + t) * 16 + r) * 64 + lane];
+            }
+            __syncthreads();
+        }
+        if (kh != 0) return;
     }
 
     const int m = m0 + c;
@@ -935,6 +975,7 @@ bool gemm_supported(int wtype) {
 
 // Grids up to this many Q4_K tiles (one per CU) split K in two
 constexpr int64_t kSplitKMaxTiles = 256;
+constexpr int kSplitQ32 = 2;  // K parts of the Q4_0 / Q5_0 / Q8_0 kernel on such grids
 
 hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
@@ -952,12 +993,22 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         const int64_t nb = (N + 63) / 64;
         const int NB = (int)(K / 32);
         const dim3 g = grid(mblocks * nb);
+        // K split in KQ32 parts (4 KQ32 waves per workgroup) for small grids
+        // whose 4-block chunks are full and a multiple of KQ32 in number
+        const bool split = mblocks * nb <= kSplitKMaxTiles && NB % (4 * kSplitQ32) == 0;
+        auto go = [&](auto k1, auto ks) {
+            if (split)
+                hipLaunchKernelGGL(ks, g, dim3(256 * kSplitQ32), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks,
+                                   (int)nb);
+            else
+                hipLaunchKernelGGL(k1, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+        };
         if (wtype == QMM_Q4_0)
-            hipLaunchKernelGGL(gemm_q32_kernel<QMM_Q4_0>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+            go(gemm_q32_kernel<QMM_Q4_0, 1>, gemm_q32_kernel<QMM_Q4_0, kSplitQ32>);
         else if (wtype == QMM_Q5_0)
-            hipLaunchKernelGGL(gemm_q32_kernel<QMM_Q5_0>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+            go(gemm_q32_kernel<QMM_Q5_0, 1>, gemm_q32_kernel<QMM_Q5_0, kSplitQ32>);
         else
-            hipLaunchKernelGGL(gemm_q32_kernel<QMM_Q8_0>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+            go(gemm_q32_kernel<QMM_Q8_0, 1>, gemm_q32_kernel<QMM_Q8_0, kSplitQ32>);
         return hipGetLastError();
     }
     if (wtype == QMM_Q6_K) {

@@ -201,7 +201,7 @@ def _q32_weights(g, wtype, M, K):
 
 @pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
 @pytest.mark.parametrize("M,N,K", [(32, 64, 128), (1, 9, 32), (31, 65, 96), (130, 100, 896), (300, 129, 1024),
-                                   (128, 512, 2048), (77, 1, 160)])
+                                   (128, 512, 2048), (77, 1, 160), (16384, 65, 512), (16400, 65, 512)])
 def test_gemm_q32_shapes(wtype, M, N, K):
     g = np.random.default_rng(M * 11 + N * 3 + K + wtype)
     W = _q32_weights(g, wtype, M, K)
