@@ -45,8 +45,11 @@ int64_t gemm_min_rows(int wtype, int64_t M) {
     switch (wtype) {
     case QMM_Q6_K: return 8;
     case QMM_Q4_K: return M > 256 * 32 ? 3 : 7;  // the narrow kernel's two-workgroups-per-CU form wins from N = 4
-    case QMM_Q4_0: case QMM_Q8_0: return 64;
-    default: return 96;  // Q5_0
+    // the Q4_0 / Q5_0 / Q8_0 GEMM takes about the same time for any N up
+    // to 512 on these shapes, while the GEMV's grows with M N
+    case QMM_Q4_0: return M > 8192 ? 24 : 48;
+    case QMM_Q8_0: return M > 8192 ? 16 : 48;
+    default: return M > 8192 ? 24 : 64;  // Q5_0
     }
 }
 

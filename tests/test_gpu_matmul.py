@@ -34,6 +34,8 @@ def make_weights(g, wt, M, K):
         return synth.q4_k_random(g, M, K)
     if wt == Q.QMM_Q6_K:
         return synth.q6_k_random(g, M, K)
+    if wt == Q.QMM_Q5_0:
+        return synth.q5_0_random(g, M, K)
     return O.quantize(O.Q8_0 if wt == Q.QMM_Q8_0 else O.Q4_0, synth.normal_f32(g, (M, K), 0.02))
 
 
@@ -124,6 +126,16 @@ def test_small_and_ragged_shapes(wt):
         x = g.standard_normal((N, K), dtype=np.float32)
         say("shape", wt, M, N, K)
         check(wt, W, x, M, N, K, what=f"type {wt} {M}x{K} N={N}")
+
+
+@pytest.mark.parametrize("wt", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
+def test_auto_choice_wide_matrix_mid_batch(wt):
+    # M > 8192 moves the GEMV/GEMM switch of these types down to N > 24 (Q8_0: 16)
+    g = np.random.default_rng(90 + wt)
+    M, N, K = 8200, 25, 512
+    W = make_weights(g, wt, M, K)
+    x = g.standard_normal((N, K), dtype=np.float32)
+    check(wt, W, x, M, N, K, algo=0, what=f"auto {M}x{K} N={N}")
 
 
 @pytest.mark.parametrize("wt", WTYPES)
