@@ -623,6 +623,14 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
 
     // this K part's chunks
     const int nper = (nch + (tail ? 1 : 0)) / KS, ch0 = kh * nper;
+    // Q5_0 issues the next chunk's loads and LDS store unconditionally
+    // (after the last chunk they re-read blocks that exist and fill a buffer
+    // nobody reads).  With a branch around them the compiler's load waits must
+    // fit both paths, and the chunk's first block then also waits for most of
+    // the next chunk's loads, of which Q5_0 has 12.  Measured at 4096x4096,
+    // N = 512: Q5_0 86.8 us against 104.8; Q4_0 and Q8_0 2-3% slower, so they
+    // keep the branch.
+    constexpr bool kAlwaysNext = WT == QMM_Q5_0;
     x_load(ch0);
     w_load(ch0);
     x_store(0);
@@ -632,7 +640,7 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
         Q32W<WT> w[CB];
 #pragma unroll
         for (int j = 0; j < CB; ++j) w[j] = wn[j];
-        if (i + 1 < nper) {
+        if (kAlwaysNext || i + 1 < nper) {
             x_load(ch + 1);
             w_load(ch + 1);
         }
@@ -656,7 +664,7 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
                 }
             }
         }
-        if (i + 1 < nper) x_store(buf ^ 1);
+        if (kAlwaysNext || i + 1 < nper) x_store(buf ^ 1);
         __syncthreads();
     }
 

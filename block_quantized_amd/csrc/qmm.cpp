@@ -48,8 +48,7 @@ int64_t gemm_min_rows(int wtype, int64_t M) {
     // the Q4_0 / Q5_0 / Q8_0 GEMM takes about the same time for any N up
     // to 512 on these shapes, while the GEMV's grows with M N
     case QMM_Q4_0: return M > 8192 ? 24 : 48;
-    case QMM_Q8_0: return M > 8192 ? 16 : 48;
-    default: return M > 8192 ? 24 : 64;  // Q5_0
+    default: return M > 8192 ? 16 : 48;  // Q8_0, Q5_0
     }
 }
 

@@ -145,7 +145,7 @@ int qmm_dequantize(int type, const void* blocks, float* out, int64_t rows, int64
  * MI355X: N > 8 for Q6_K; N > 7 for Q4_K, or N > 3 when M > 8192 (Q4_K
  * with N <= 32 takes narrow MFMA kernels, on 32- or 16-row tiles, that
  * split K over the waves of a workgroup); for Q4_0, Q8_0 and Q5_0, N > 48,
- * 48 and 64, or N > 24, 16 and 24 when M > 8192. */
+ * or N > 24 (Q4_0) and N > 16 (Q8_0, Q5_0) when M > 8192. */
 int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y,
                 int64_t M, int64_t N, int64_t K, void* stream);
 
