@@ -103,7 +103,10 @@ def test_hand_q4_k(golden):
     x[0:4] = np.array([1.0], np.float32).view(np.uint8)
     x[4:260] = 1
     x[260:] = np.full(16, 16, np.int16).view(np.uint8)
-    assert O.mul_mat(O.Q4_K, blk, x, 1, 1, 256)[0][0, 0] == h["dot_with_q8_k_d1_all_ones"]
+    y, T = O.mul_mat(O.Q4_K, blk, x, 1, 1, 256)
+    assert y[0, 0] == h["dot_with_q8_k_d1_all_ones"]
+    # the tolerance's term sum counts the scale part and the min part apart
+    assert T[0, 0] == h["term_sum_with_q8_k_d1_all_ones"]
     assert O.mul_mat_blockwise(O.Q4_K, blk, x, 1, 1, 256)[0, 0] == h["dot_with_q8_k_d1_all_ones"]
     hb = h["high_bits_case"]
     blk[4 + 0] = hb["scales_0"]

@@ -156,12 +156,14 @@ def test_integer_cases_match_int_matmul(seed):
     K = 32 * int(g.integers(1, 17))
     qw = g.integers(-128, 128, (M, K))
     qx = g.integers(-127, 128, (N, K))
-    y, _ = O.mul_mat(O.Q8_0, enc_q8_0(qw), enc_q8_0(qx), M, N, K)
+    y, T = O.mul_mat(O.Q8_0, enc_q8_0(qw), enc_q8_0(qx), M, N, K)
     assert np.array_equal(y, (qx @ qw.T).astype(np.float64))
+    assert np.array_equal(T, (np.abs(qx) @ np.abs(qw).T).astype(np.float64))
     # Q4_0: w = q - 8
     qn = g.integers(0, 16, (M, K))
-    y, _ = O.mul_mat(O.Q4_0, enc_q4_0(qn), enc_q8_0(qx), M, N, K)
+    y, T = O.mul_mat(O.Q4_0, enc_q4_0(qn), enc_q8_0(qx), M, N, K)
     assert np.array_equal(y, (qx @ (qn - 8).T).astype(np.float64))
+    assert np.array_equal(T, (np.abs(qx) @ np.abs(qn - 8).T).astype(np.float64))
     # Q5_0: w = q - 16, q = low nibble | fifth bit << 4
     q5 = g.integers(0, 32, (M, K))
     y, _ = O.mul_mat(O.Q5_0, enc_q5_0(q5), enc_q8_0(qx), M, N, K)
@@ -177,8 +179,11 @@ def test_integer_cases_match_int_matmul(seed):
     qx = g.integers(-127, 128, (N, K))
     W = enc_q4_k(q, sc, mn)
     X = enc_q8_k(qx)
-    y, _ = O.mul_mat(O.Q4_K, W, X, M, N, K)
+    y, T = O.mul_mat(O.Q4_K, W, X, M, N, K)
     assert np.array_equal(y, (qx @ w.T).astype(np.float64))
+    # term sum: the scale part sc q and the min part m count separately
+    t_w = np.repeat(sc.reshape(M, -1), 32, axis=1) * q + np.repeat(mn.reshape(M, -1), 32, axis=1)
+    assert np.array_equal(T, (np.abs(qx) @ t_w.T).astype(np.float64))
     assert np.array_equal(O.mul_mat_blockwise(O.Q4_K, W, X, M, N, K), (qx @ w.T).astype(np.float64))
     assert np.array_equal(O.dequantize(O.Q4_K, W, M, K), w.astype(np.float32))
     # Q6_K with d = 1 and random int8 scales over the full range: w = sc (q - 32)
@@ -186,8 +191,9 @@ def test_integer_cases_match_int_matmul(seed):
     sc6 = g.integers(-128, 128, (M, nb, 16))
     w6 = np.repeat(sc6.reshape(M, -1), 16, axis=1) * (q6 - 32)
     W6 = enc_q6_k(q6, sc6)
-    y, _ = O.mul_mat(O.Q6_K, W6, X, M, N, K)
+    y, T = O.mul_mat(O.Q6_K, W6, X, M, N, K)
     assert np.array_equal(y, (qx @ w6.T).astype(np.float64))
+    assert np.array_equal(T, (np.abs(qx) @ np.abs(w6).T).astype(np.float64))
     assert np.array_equal(O.mul_mat_blockwise(O.Q6_K, W6, X, M, N, K), (qx @ w6.T).astype(np.float64))
     assert np.array_equal(O.dequantize(O.Q6_K, W6, M, K), w6.astype(np.float32))
 

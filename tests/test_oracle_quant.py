@@ -225,6 +225,30 @@ def test_q4_0_encoder():
     assert np.all(w[5 * 64] == 0)
 
 
+def _q4_0_codes(b):
+    bl = b.reshape(-1, 18)
+    qs = bl[:, 2:]
+    return bl[:, 0:2].copy().view(np.uint16)[:, 0], np.concatenate([qs & 15, qs >> 4], axis=1)
+
+
+def test_hand_q4_0_encoder_ties(golden):
+    h = golden("hand_blocks.json")["q4_0_encoder_ties"]
+    b = O.quantize(O.Q4_0, np.array(h["x"], np.float32))
+    d16, q = _q4_0_codes(b)
+    assert d16[0] == h["d_fp16_bits"]
+    assert q[0].tolist() == h["q"]
+    assert b.reshape(-1)[2:18].tolist() == h["qs_bytes"]
+    assert q[0].tolist() != h["q_if_ties_to_even"]
+
+
+def test_hand_q4_0_encoder_nan(golden):
+    h = golden("hand_blocks.json")["q4_0_encoder_nan"]
+    x = np.array([np.nan if v == "nan" else v for v in h["x"]], np.float32)
+    d16, q = _q4_0_codes(O.quantize(O.Q4_0, x))
+    assert d16[0] == h["d_fp16_bits"]
+    assert q[0].tolist() == h["q"]
+
+
 def test_reciprocal_of_d_is_what_multiplies():
     # id is 1/d with d = amax/127 already rounded to fp32, not 127/amax.  Find
     # amax values where the two differ in fp32, and values x whose products
