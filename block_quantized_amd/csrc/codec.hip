@@ -98,9 +98,12 @@ __global__ __launch_bounds__(256) void quantize_q4_0_kernel(const float* __restr
     const int sub = threadIdx.x & 7;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (b < nblocks) v = reinterpret_cast<const float4*>(x)[t];
-    // first maximum of |x| within the lane, then across the 8 lanes
-    float ba = fabsf(v.x), bm = v.x;
+    // first maximum of |x| within the lane, then across the 8 lanes; every
+    // element, the first included, must beat the running maximum (from 0)
+    // with a strict >, so NaN never wins and an all-zero block keeps m = 0
+    float ba = 0.0f, bm = 0.0f;
     int bi = 0;
+    if (fabsf(v.x) > ba) { ba = fabsf(v.x); bm = v.x; }
     if (fabsf(v.y) > ba) { ba = fabsf(v.y); bm = v.y; bi = 1; }
     if (fabsf(v.z) > ba) { ba = fabsf(v.z); bm = v.z; bi = 2; }
     if (fabsf(v.w) > ba) { ba = fabsf(v.w); bm = v.w; bi = 3; }
@@ -279,12 +282,11 @@ hipError_t launch_quantize(int dst, const float* x, void* out, int64_t rows, int
     const int64_t nb = rows * (K / block_size(dst));
     uint8_t* o = static_cast<uint8_t*>(out);
     switch (dst) {
-    case QMM_Q8_0: hipLaunchKernelGGL(quantize_q8_0_kernel, dim3(grid_for(nb * 8)), dim3(256), 0, s, x, o, nb); break;
-    case QMM_Q8_K: hipLaunchKernelGGL(quantize_q8_k_kernel, dim3(grid_for(nb * 64)), dim3(256), 0, s, x, o, nb); break;
-    case QMM_Q4_0: hipLaunchKernelGGL(quantize_q4_0_kernel, dim3(grid_for(nb * 8)), dim3(256), 0, s, x, o, nb); break;
+    case QMM_Q8_0: return launch(quantize_q8_0_kernel, dim3(grid_for(nb * 8)), dim3(256), 0, s, x, o, nb);
+    case QMM_Q8_K: return launch(quantize_q8_k_kernel, dim3(grid_for(nb * 64)), dim3(256), 0, s, x, o, nb);
+    case QMM_Q4_0: return launch(quantize_q4_0_kernel, dim3(grid_for(nb * 8)), dim3(256), 0, s, x, o, nb);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_dequantize(int t, const void* blocks, float* out, int64_t rows, int64_t K, hipStream_t s) {
@@ -292,15 +294,14 @@ hipError_t launch_dequantize(int t, const void* blocks, float* out, int64_t rows
     const uint8_t* w = static_cast<const uint8_t*>(blocks);
     const dim3 g(grid_for(nq)), blk(256);
     switch (t) {
-    case QMM_Q4_0: hipLaunchKernelGGL(dequant_q4_0_kernel, g, blk, 0, s, w, out, nq); break;
-    case QMM_Q8_0: hipLaunchKernelGGL(dequant_q8_0_kernel, g, blk, 0, s, w, out, nq); break;
-    case QMM_Q5_0: hipLaunchKernelGGL(dequant_q5_0_kernel, g, blk, 0, s, w, out, nq); break;
-    case QMM_Q4_K: hipLaunchKernelGGL(dequant_q4_k_kernel, g, blk, 0, s, w, out, nq); break;
-    case QMM_Q6_K: hipLaunchKernelGGL(dequant_q6_k_kernel, g, blk, 0, s, w, out, nq); break;
-    case QMM_Q8_K: hipLaunchKernelGGL(dequant_q8_k_kernel, g, blk, 0, s, w, out, nq); break;
+    case QMM_Q4_0: return launch(dequant_q4_0_kernel, g, blk, 0, s, w, out, nq);
+    case QMM_Q8_0: return launch(dequant_q8_0_kernel, g, blk, 0, s, w, out, nq);
+    case QMM_Q5_0: return launch(dequant_q5_0_kernel, g, blk, 0, s, w, out, nq);
+    case QMM_Q4_K: return launch(dequant_q4_k_kernel, g, blk, 0, s, w, out, nq);
+    case QMM_Q6_K: return launch(dequant_q6_k_kernel, g, blk, 0, s, w, out, nq);
+    case QMM_Q8_K: return launch(dequant_q8_k_kernel, g, blk, 0, s, w, out, nq);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace qmm

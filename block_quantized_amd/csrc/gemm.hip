@@ -177,14 +177,18 @@ __global__ __launch_bounds__(256 * KS, 2 / KS) void gemm_q4k_kernel(const uint8_
     const unsigned vo_sums = (unsigned)((lane >> 1) * rowsB + 260 + 16 * (lane & 1));  // 32 rows x 2 halves
     const unsigned vo_dx = (unsigned)(lane * rowsB);                                   // row l's scale
     static_assert(BN / 4 <= 32 && BN / 4 * 3 + 64 <= BN + 48, "the sums and scales copies fit the tile");
+    // The row part of every copy's address is in the lane offset, which the
+    // descriptor's range check covers (the scalar offset, the super-block
+    // here, is not range-checked on gfx9-family chips), so rows at or past
+    // N read as zeros and no copy reaches past the workgroup's rows of X.
     auto x_copy = [&](XTile<BN>& T, int sb) {
-        const int sbB = sb * kQ8_KBytes;
+        const unsigned sbB = (unsigned)(sb * kQ8_KBytes);
         const int r0 = BN / 4 * wave;
 #pragma unroll
         for (int i = 0; i < BN / 16; ++i)
-            copy16_to_lds(xr, &T.codes[4 * (wave + 4 * i)][0], vo_codes, (unsigned)(16 * i * rowsB + sbB));
-        copy16_to_lds(xr, &T.sums[r0][0], vo_sums, (unsigned)(r0 * rowsB + sbB));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.dx[r0], 4, vo_dx, (unsigned)(r0 * rowsB + sbB), 0, 0);
+            copy16_to_lds(xr, &T.codes[4 * (wave + 4 * i)][0], vo_codes + (unsigned)(16 * i * rowsB), sbB);
+        copy16_to_lds(xr, &T.sums[r0][0], vo_sums + (unsigned)(r0 * rowsB), sbB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.dx[r0], 4, vo_dx + (unsigned)(r0 * rowsB), sbB, 0, 0);
     };
     // ---- weights: header + this lane's halves of the four nibble-pair chunks
     // two super-blocks of weights in flight (the next and the one after): one
@@ -1006,64 +1010,55 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         const bool split = mblocks * nb <= kSplitKMaxTiles && NB % (4 * kSplitQ32) == 0;
         auto go = [&](auto k1, auto ks) {
             if (split)
-                hipLaunchKernelGGL(ks, g, dim3(256 * kSplitQ32), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks,
-                                   (int)nb);
-            else
-                hipLaunchKernelGGL(k1, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+                return launch(ks, g, dim3(256 * kSplitQ32), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks,
+                              (int)nb);
+            return launch(k1, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
         };
-        if (wtype == QMM_Q4_0)
-            go(gemm_q32_kernel<QMM_Q4_0, 1>, gemm_q32_kernel<QMM_Q4_0, kSplitQ32>);
-        else if (wtype == QMM_Q5_0)
-            go(gemm_q32_kernel<QMM_Q5_0, 1>, gemm_q32_kernel<QMM_Q5_0, kSplitQ32>);
-        else
-            go(gemm_q32_kernel<QMM_Q8_0, 1>, gemm_q32_kernel<QMM_Q8_0, kSplitQ32>);
-        return hipGetLastError();
+        if (wtype == QMM_Q4_0) return go(gemm_q32_kernel<QMM_Q4_0, 1>, gemm_q32_kernel<QMM_Q4_0, kSplitQ32>);
+        if (wtype == QMM_Q5_0) return go(gemm_q32_kernel<QMM_Q5_0, 1>, gemm_q32_kernel<QMM_Q5_0, kSplitQ32>);
+        return go(gemm_q32_kernel<QMM_Q8_0, 1>, gemm_q32_kernel<QMM_Q8_0, kSplitQ32>);
     }
     if (wtype == QMM_Q6_K) {
         // bound by streaming W: one 32-row activation tile per workgroup up to
         // N = 32 (W read once), wider tiles beyond
         if (N <= 32) {
-            hipLaunchKernelGGL(gemm_q6k_kernel<1>, grid(mblocks), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
+            return launch(gemm_q6k_kernel<1>, grid(mblocks), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
                                (int)mblocks, 1);
         } else {
             const int64_t nb = (N + 63) / 64;
-            hipLaunchKernelGGL(gemm_q6k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
+            return launch(gemm_q6k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
                                (int)mblocks, (int)nb);
         }
-        return hipGetLastError();
     }
     if (N <= 16 && M <= 8192) {  // 16-row tiles: enough workgroups for every CU
         const int64_t tiles = (M + 15) / 16;
         if (tiles <= 256)
-            hipLaunchKernelGGL(gemm_narrow16_q4k_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, s, w, x, y, (int)M,
+            return launch(gemm_narrow16_q4k_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, s, w, x, y, (int)M,
                                (int)N, SB);
         else
-            hipLaunchKernelGGL(gemm_narrow16_q4k_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, s, w, x, y, (int)M,
+            return launch(gemm_narrow16_q4k_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, s, w, x, y, (int)M,
                                (int)N, SB);
-        return hipGetLastError();
     }
     if (N <= 32) {
         // 8 waves per workgroup (one workgroup per CU) while the row tiles fit
         // in one pass over the CUs; past that, 4 (two workgroups per CU)
         const int64_t tiles = (M + 31) / 32;
         if (tiles <= 256)
-            hipLaunchKernelGGL(gemm_narrow_q4k_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, s, w, x, y, (int)M,
+            return launch(gemm_narrow_q4k_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, s, w, x, y, (int)M,
                                (int)N, SB);
         else
-            hipLaunchKernelGGL(gemm_narrow_q4k_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, s, w, x, y, (int)M,
+            return launch(gemm_narrow_q4k_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, s, w, x, y, (int)M,
                                (int)N, SB);
-        return hipGetLastError();
     }
     // 64 activation rows per workgroup: two waves per SIMD fit (the 128-row
     // tile needs one SIMD's registers per wave), measured faster at every size
     const int64_t nb = (N + 63) / 64;
     if (mblocks * nb <= kSplitKMaxTiles && SB % 2 == 0)  // K split in two: 8 waves per workgroup
-        hipLaunchKernelGGL((gemm_q4k_kernel<2, 2>), grid(mblocks * nb), dim3(512), 0, s, w, x, y, (int)M, (int)N,
+        return launch(gemm_q4k_kernel<2, 2>, grid(mblocks * nb), dim3(512), 0, s, w, x, y, (int)M, (int)N,
                            SB, (int)mblocks, (int)nb);
     else
-        hipLaunchKernelGGL((gemm_q4k_kernel<2, 1>), grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N,
+        return launch(gemm_q4k_kernel<2, 1>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N,
                            SB, (int)mblocks, (int)nb);
-    return hipGetLastError();
 }
 
 }  // namespace qmm

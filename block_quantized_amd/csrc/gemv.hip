@@ -865,8 +865,7 @@ hipError_t launch_one(const GemvArgs& a, size_t lds, int wpg, hipStream_t s) {
     const int64_t need = (a.nwork + wpg - 1) / wpg;
     const int64_t cap = (int64_t)di.cus * (per_cu > 0 ? per_cu : 1);
     const int grid = (int)(need < cap ? need : cap);
-    hipLaunchKernelGGL((gemv_kernel<WT, NC, XF>), dim3(grid), dim3(wpg * 64), lds, s, a);
-    return hipGetLastError();
+    return launch(gemv_kernel<WT, NC, XF>, dim3(grid), dim3(wpg * 64), lds, s, a);
 }
 
 template <int WT, bool XF>
@@ -937,11 +936,10 @@ hipError_t rowwave(int wtype, const void* W, const void* xq, float* y, int64_t M
     const dim3 g((unsigned)((M + 3) / 4)), b(256);
     const uint8_t* w = static_cast<const uint8_t*>(W);
     const uint8_t* x = static_cast<const uint8_t*>(xq);
-    if (wtype == QMM_Q4_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q4_0>, g, b, 0, s, w, x, y, M, (int)N, K);
-    else if (wtype == QMM_Q8_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q8_0>, g, b, 0, s, w, x, y, M, (int)N, K);
-    else if (wtype == QMM_Q5_0) hipLaunchKernelGGL(gemv_rowwave_kernel<QMM_Q5_0>, g, b, 0, s, w, x, y, M, (int)N, K);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (wtype == QMM_Q4_0) return launch(gemv_rowwave_kernel<QMM_Q4_0>, g, b, 0, s, w, x, y, M, (int)N, K);
+    if (wtype == QMM_Q8_0) return launch(gemv_rowwave_kernel<QMM_Q8_0>, g, b, 0, s, w, x, y, M, (int)N, K);
+    if (wtype == QMM_Q5_0) return launch(gemv_rowwave_kernel<QMM_Q5_0>, g, b, 0, s, w, x, y, M, (int)N, K);
+    return hipErrorInvalidValue;
 }
 
 bool needs_rowwave(int wtype, int64_t K) {

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
 #include <type_traits>
 
 #include "../../include/qmm.h"
@@ -53,6 +54,22 @@ __device__ __forceinline__ void rtn_scale(float amax, float& d, float& id) {
     id = (d != 0.0f) ? 1.0f / d : 0.0f;
 }
 #endif
+
+// Launches kernel k and returns the status of this launch alone.  Unlike
+// hipGetLastError() after a triple-chevron launch, an error left by an
+// earlier, unrelated HIP call in the same thread is neither reported nor
+// cleared.  The arguments are converted to the kernel's parameter types.
+template <typename... P, typename... A>
+hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, A... a) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<std::decay_t<P>...> args{static_cast<std::decay_t<P>>(a)...};
+    void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1] = {};
+    std::apply([&ptrs](auto&... e) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void*>(&e)), ...);
+    }, args);
+    return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, lds, s);
+}
 
 // ---- launchers (return hipError_t of the launch) ----
 hipError_t launch_quantize(int dst, const float* x, void* out, int64_t rows, int64_t K, hipStream_t s);

@@ -91,6 +91,29 @@ def test_quantize_q4_0_weights():
     assert_bytes_equal(gpu_quantize(Q.QMM_Q4_0, z, act=False), O.quantize(O.Q4_0, z), "signed zero")
 
 
+def test_quantize_q4_0_nan_is_never_the_maximum():
+    # NaN at the first element of a lane's four (elements 0, 4k) and elsewhere;
+    # the magnitude search skips NaN, as the oracle's strict '>' does
+    g = np.random.default_rng(13)
+    x = g.standard_normal((6, 64), dtype=np.float32)
+    x[0, 0] = np.nan
+    x[1, 4] = np.nan
+    x[2, 28] = np.nan
+    x[3, 0:32] = np.nan              # a block of NaN only: m = 0, every code 8
+    x[4, 32] = np.nan
+    x[4, 33] = -np.inf
+    x[5, 16] = np.nan
+    x[5, 0] = 1e-40
+    assert_bytes_equal(gpu_quantize(Q.QMM_Q4_0, x, act=False), O.quantize(O.Q4_0, x), "NaN inputs")
+
+
+def test_quantize_q4_0_hand_block(golden):
+    h = golden("hand_blocks.json")["q4_0_encoder_ties"]
+    b = gpu_quantize(Q.QMM_Q4_0, np.array(h["x"], np.float32)[None, :], act=False).reshape(-1)
+    assert int(b[0]) | (int(b[1]) << 8) == h["d_fp16_bits"]
+    assert b[2:18].tolist() == h["qs_bytes"]
+
+
 def random_blocks(t, rows, K, g):
     """Random block bytes with finite scales (NaN/Inf scales are no parity case)."""
     nb = K // O.BLOCK_SIZE[t]

@@ -14,13 +14,13 @@ import torch
 import block_quantized_amd as Q
 import oracle as O
 import synth
-from gpu_util import assert_within_tolerance, to_cpu, to_gpu
+from gpu_util import assert_within_tolerance, run_product, tile_rows, to_cpu, to_gpu
 
 pytestmark = pytest.mark.gpu
 
 
 def run(W, xq, M, N, K, algo=2):
-    return to_cpu(Q.mul_mat(Q.QMM_Q4_K, to_gpu(W), to_gpu(xq), M, N, K, algo=algo))
+    return run_product(Q.QMM_Q4_K, W, xq, M, N, K, algo=algo)
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 256), (1, 9, 256), (31, 33, 512), (130, 100, 768), (300, 129, 1024),
@@ -121,7 +121,7 @@ def test_gemm_q4k_narrow_deterministic_and_in_bounds(M, N, K):
 # ------------------------------------------------------------------ Q6_K
 
 def run_q6k(W, xq, M, N, K, algo=2):
-    return to_cpu(Q.mul_mat(Q.QMM_Q6_K, to_gpu(W), to_gpu(xq), M, N, K, algo=algo))
+    return run_product(Q.QMM_Q6_K, W, xq, M, N, K, algo=algo)
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 256), (1, 9, 256), (31, 33, 512), (130, 100, 768), (300, 32, 2048),
@@ -161,16 +161,16 @@ def test_gemm_q6k_extreme_scales():
 
 def test_gemm_q6k_head_sampled():
     # the 128256 x 4096 output head at batch 32, as the automatic choice runs
-    # it, checked on sampled rows against the oracle
+    # it: every output written, one row of every 32-row tile against the oracle
     g = np.random.default_rng(0)
     M, K = 128256, 4096
     N = 32
     W = synth.q6_k_random(g, M, K)
     xq = O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32))
-    y = to_cpu(Q.mul_mat(Q.QMM_Q6_K, to_gpu(W), to_gpu(xq), M, N, K))
-    rows = np.unique(np.concatenate([np.arange(8), M - 1 - np.arange(8), g.integers(0, M, 48)]))
+    y = run_product(Q.QMM_Q6_K, W, xq, M, N, K)
+    rows = np.unique(np.concatenate([np.arange(8), M - 1 - np.arange(8), tile_rows(M, seed=1)]))
     y_ref, T = O.mul_mat(O.Q6_K, np.ascontiguousarray(W[rows]), xq, len(rows), N, K)
-    assert_within_tolerance(y[:, rows], y_ref, T, what="Q6_K head N=32 (sampled rows)")
+    assert_within_tolerance(y[:, rows], y_ref, T, what="Q6_K head N=32 (one row per 32-row tile)")
 
 
 def test_gemm_q6k_deterministic_in_bounds_and_matches_gemv():
@@ -207,7 +207,7 @@ def test_gemm_q32_shapes(wtype, M, N, K):
     W = _q32_weights(g, wtype, M, K)
     xq = O.quantize(O.Q8_0, g.standard_normal((N, K), dtype=np.float32))
     print("gemm q32", wtype, M, N, K, flush=True)
-    y = to_cpu(Q.mul_mat(wtype, to_gpu(W), to_gpu(xq), M, N, K, algo=2))
+    y = run_product(wtype, W, xq, M, N, K, algo=2)
     ow = {Q.QMM_Q4_0: O.Q4_0, Q.QMM_Q5_0: O.Q5_0, Q.QMM_Q8_0: O.Q8_0}[wtype]
     y_ref, T = O.mul_mat(ow, W, xq, M, N, K)
     assert_within_tolerance(y, y_ref, T, what=f"GEMM type {wtype} {M}x{K} N={N}")
@@ -245,15 +245,15 @@ def test_gemm_q32_extremes_and_determinism(wtype):
 
 @pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
 def test_gemm_q32_bench_size_sampled(wtype):
-    # the 4096 x 4096, N = 512 product the benchmark times (automatic choice),
-    # checked on sampled weight rows against the oracle
+    # the 4096 x 4096, N = 512 product the benchmark times (automatic choice):
+    # every output written, one row of every 32-row tile against the oracle
     M, N, K = 4096, 512, 4096
     g = synth.rng(0)
     W = _q32_weights(g, wtype, M, K)
     xq = O.quantize(O.Q8_0, synth.normal_f32(g, (N, K), 1.0))
     print("gemm q32 bench size", wtype, flush=True)
-    y = to_cpu(Q.mul_mat(wtype, to_gpu(W), to_gpu(xq), M, N, K))
-    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], g.integers(0, M, 40)]))
+    y = run_product(wtype, W, xq, M, N, K)
+    rows = tile_rows(M, seed=2)
     ow = {Q.QMM_Q4_0: O.Q4_0, Q.QMM_Q5_0: O.Q5_0, Q.QMM_Q8_0: O.Q8_0}[wtype]
     y_ref, T = O.mul_mat(ow, np.ascontiguousarray(W[rows]), xq, len(rows), N, K)
     assert_within_tolerance(y[:, rows], y_ref, T, what=f"GEMM type {wtype} 4096x4096 N=512")

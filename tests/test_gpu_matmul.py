@@ -6,7 +6,8 @@ B^T) = C^T), computed per block as an integer dot scaled by the block scales
 weights against quantized activations').  The GPU result must satisfy
 |y - y_ref| <= 1e-5 * T per output, with y_ref and T from the CPU oracle
 (T = sum of |terms|; for Q4_K the scale and min parts are counted apart).
-Full workload sizes are checked on sampled rows the oracle computes one by one.
+Full workload sizes are checked on one row of every 32-row tile (all columns),
+which the oracle computes one by one, and every output must have been written.
 """
 import sys
 
@@ -17,7 +18,7 @@ import torch
 import block_quantized_amd as Q
 import oracle as O
 import synth
-from gpu_util import assert_within_tolerance, to_cpu, to_gpu
+from gpu_util import assert_within_tolerance, run_product, tile_rows, to_cpu, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -40,12 +41,11 @@ def make_weights(g, wt, M, K):
 
 
 def check(wt, W, x, M, N, K, rows=None, algo=0, what=""):
-    """Run the GPU product on the full matrix; compare all rows or `rows`."""
+    """Run the GPU product on the full matrix; compare all rows or `rows`
+    (all N columns of each)."""
     xt = O.VEC_DOT_TYPE[wt]
     xq = O.quantize(xt, x)
-    Wg = to_gpu(W)
-    xg = to_gpu(xq)
-    y = to_cpu(Q.mul_mat(wt, Wg, xg, M, N, K, algo=algo))
+    y = run_product(wt, W, xq, M, N, K, algo=algo)  # every output written, nothing past y
     if rows is None:
         y_ref, T = O.mul_mat(wt, W, xq, M, N, K)
         assert_within_tolerance(y, y_ref, T, what=what)
@@ -54,12 +54,6 @@ def check(wt, W, x, M, N, K, rows=None, algo=0, what=""):
         y_ref, T = O.mul_mat(wt, Ws, xq, len(rows), N, K)
         assert_within_tolerance(y[:, rows], y_ref, T, what=what)
     return y
-
-
-def sample_rows(M, n=96, seed=0):
-    g = np.random.default_rng(seed)
-    r = np.unique(np.concatenate([[0, 1, M - 2, M - 1], g.integers(0, M, n)]))
-    return r[(r >= 0) & (r < M)]
 
 
 # ----------------------------------------------------- the five workloads
@@ -97,7 +91,7 @@ def test_config_q4_k_prefill_512(M):
     W = synth.q4_k_random(g, M, 4096)
     x = synth.normal_f32(g, (512, 4096), 1.0)
     say("Q4_K prefill", M)
-    check(Q.QMM_Q4_K, W, x, M, 512, 4096, rows=sample_rows(M, 48), what=f"Q4_K {M}x4096 N=512")
+    check(Q.QMM_Q4_K, W, x, M, 512, 4096, rows=tile_rows(M), what=f"Q4_K {M}x4096 N=512")
 
 
 @pytest.mark.parametrize("N", [1, 32])
@@ -107,7 +101,7 @@ def test_config_q6_k_head(N):
     W = synth.q6_k_random(g, M, K)
     x = synth.normal_f32(g, (N, K), 1.0)
     say("Q6_K head N", N)
-    check(Q.QMM_Q6_K, W, x, M, N, K, rows=None if N == 1 else sample_rows(M, 256),
+    check(Q.QMM_Q6_K, W, x, M, N, K, rows=None if N == 1 else tile_rows(M),
           what=f"Q6_K head N={N}")
 
 
