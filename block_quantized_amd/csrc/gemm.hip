@@ -97,226 +97,350 @@ __device__ __forceinline__ uint32_t mul_bytes(uint32_t v, uint32_t s) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Copies 16 bytes per lane from a buffer into LDS (lane l's bytes land at
-// lds + 16 l) with no VGPR round trip.  The 16-byte form is gfx950's; the
-// host pass of the compiler does not know it, so it sees an empty body.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voff, unsigned soff) {
+// ---------------------------------------------------------------- Q4_K
+// A wave computes 32 weight rows x 32*TN activation rows (TN result tiles of
+// v_mfma_i32_32x32x32_i8).  The weight planes of a sub-block are built once
+// per wave and feed all TN tiles, so the VALU work of building them is
+// spread over TN matrix instructions.  To keep one int32 accumulator per
+// tile, the two planes run one after the other within each super-block: the
+// (sc >> 3) plane of all eight sub-blocks, then the accumulator times 8
+// (a shift), then the (sc & 7) plane on top of it, which leaves
+// sum_j sc_j P_j exact in the accumulator.
+//
+// A workgroup is KS groups of W waves.  The W waves of a group take
+// consecutive 32-row blocks of W and share one activation tile in LDS; the
+// KS groups take consecutive ranges of super-blocks (K split), and their
+// partial sums are added through LDS in a fixed order at the end.  All
+// operands go through LDS, read one super-block ahead.
+//
+// Per super-block a wave issues about as much VALU work (the planes, and the
+// fp32 epilogue, whose scales change every super-block) as matrix work, and
+// on gfx950 the two overlap only in part, within a wave or across the waves
+// of a SIMD: this, not the matrix cores, bounds the kernel.
+
+// One super-block of operands in LDS for a K part: the 32*TN activation
+// rows' codes (row n's 256 codes as 16 chunks of 16 bytes, chunk q at
+// position q ^ (n & 15), so that the operand reads of 16 consecutive rows at
+// one chunk cover all 64 LDS banks), and each wave's 32 weight rows (144
+// bytes each, as in memory).  Double-buffered.
+// (A wave's weights arrive as 5 reads of 64 x 16 bytes, so its region is
+// 5120 bytes: the last 512 receive a repeat of the first 32 chunks.)
+constexpr int kQ4KWaveW = 5 * 64 * 16;
+template <int TN, int W, int KS, bool WLDS>
+struct Q4KStage {
+    uint8_t codes[KS][32 * TN][256];
+    uint8_t w[KS][W][WLDS ? kQ4KWaveW : 16];
+};
+// The activation rows' 16 sums and scale for one super-block, double-buffered.
+template <int TN, int KS>
+struct Q4KSums {
+    int16_t sums[KS][32 * TN][16];
+    float dx[KS][32 * TN];
+};
+
+// The compiler must assume v changed here (emits no instruction).
+__device__ __forceinline__ void opaque(uint4& v) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 #endif
 }
 
-// Activation tile of one super-block in LDS: row n's 256 codes as 16 chunks
-// of 16 bytes, chunk q stored at position q ^ (n & 15), so that the operand
-// reads of 16 consecutive rows at one chunk fall on all 64 LDS banks; its 16
-// sums; its scale.  The sums and scales have room for 48 more rows: every
-// wave copies rows past its own share (the same bytes as the wave that owns
-// them), so that all waves issue the same copies with no branch.
-template <int BN>
-struct XTile {
-    uint8_t codes[BN][256];
-    int16_t sums[BN + 48][16];
-    float dx[BN + 48];
-};
+// No instruction is moved across this point by the compiler's scheduler.
+__device__ __forceinline__ void sched_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+}
 
-// The activation tile is copied from global memory straight into LDS
-// (buffer_load ... lds: no VGPR round trip, no VALU), one super-block
-// ahead.  The two tiles are distinct LDS objects, so the compiler can see
-// that reading one tile never waits for the copy into the other; the
-// barrier that ends each super-block waits for the copy.  The buffer descriptor covers only this workgroup's
-// activation rows: rows past N read as zeros (their outputs are not stored).
-//
-// KS = 2 splits K between two groups of 4 waves (the first and second half
-// of the super-blocks, each with its own pair of tiles); the second group
-// hands its partial sums to the first through LDS at the end, which adds
-// them in a fixed order.  It doubles the waves of a grid that has no more
-// workgroups than the GPU has CUs.
-template <int BN, int KS>
-struct XTiles {
-    XTile<BN> h[KS];
-};
+// byte k of w in both 16-bit halves: (w.k, 0, w.k, 0)
+__device__ __forceinline__ uint32_t byte_u16x2(uint32_t w, int k) {
+    return __builtin_amdgcn_perm(0u, w, (0x0Cu << 24) | ((uint32_t)k << 16) | (0x0Cu << 8) | (uint32_t)k);
+}
+// four bytes (each <= 15) times the 16-bit pair s2 = (s, 0, s, 0), s <= 7:
+// every product (<= 105) stays in its byte
+__device__ __forceinline__ int mul_bytes2(uint32_t v, uint32_t s2) {
+    return (int)__builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v) * __builtin_bit_cast(u16x2, s2));
+}
 
-template <int NT, int KS>
-__global__ __launch_bounds__(256 * KS, 2 / KS) void gemm_q4k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int N, int SB,
-                                                       int mblk, int nblk) {
-    constexpr int BN = NT * 32;  // activation rows per workgroup
-    static_assert(BN % 32 == 0 && BN <= 64, "staging assumes 4 waves and at most 64 rows");
-    static_assert(KS == 1 || KS == 2, "K is split in at most two");
-    __shared__ __attribute__((aligned(16))) XTiles<BN, KS> tiles0;
-    __shared__ __attribute__((aligned(16))) XTiles<BN, KS> tiles1;
+template <int TN, int W, int KS, int WPE>
+__global__ __launch_bounds__(64 * W * KS) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void gemm_q4k_kernel(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ X, float* __restrict__ Y,
+                     int M, int N, int SB, int mblk, int nblk) {
+    constexpr int BN = 32 * TN;  // activation rows per workgroup
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8, "waves per K part");
+    static_assert(TN == 2 || TN == 4, "tiles per wave");
+    // Weights through LDS (coalesced reads of whole rows) for four tiles per
+    // wave; with two, each lane reads its own row's header and nibble pairs
+    // straight into registers (fewer LDS operations, registers to spare).
+    constexpr bool kWLDS = TN == 4;
+    __shared__ __attribute__((aligned(16))) Q4KStage<TN, W, KS, kWLDS> st[2];
+    __shared__ __attribute__((aligned(16))) Q4KSums<TN, KS> sd[2];
 
-    // wave-uniform (scalar) wave index: the copies' LDS addresses go to M0
-    const int tid = threadIdx.x, lane = tid & 63, wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave = wave_all & 3, kh = wave_all >> 2;  // row wave, K part
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
+    const int wave = wave_all % W, kp = wave_all / W;
     const int c = lane & 31, h = lane >> 5;
-    XTile<BN>& tile0 = tiles0.h[kh];
-    XTile<BN>& tile1 = tiles1.h[kh];
-    // this K part's super-blocks (the launcher makes SB a multiple of KS)
-    const int sb0 = kh * (SB / KS), sb1 = sb0 + SB / KS;
     int rb, cb;
     if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
-    const int m0 = rb * 128 + wave * 32;
+    const int m0 = rb * (32 * W) + 32 * wave;
     const int n0 = cb * BN;
-    const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
-    const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
-    const int hsw = h ^ (c & 15);  // chunk 2j + h of row 32t + c sits at position (2j) ^ hsw
+    const int nsb = SB / KS, sb0 = kp * nsb;  // this K part's super-blocks (SB % KS == 0)
 
-    // ---- activation copies (per lane: constant offsets; per super-block: scalar offsets)
-    const int rowsB = SB * kQ8_KBytes;  // bytes of one activation row
-    const int nrows = min(BN, N - n0);
+    // ---- operand reads.  One buffer descriptor for the workgroup's activation
+    // rows that exist and one for the wave's weight rows that exist; every
+    // read's whole offset (row, super-block, bytes within the record) is in
+    // the lane offset, which the descriptor's range check covers (the scalar
+    // offset is 0), so rows at or past N (or M) read as zeros and no read
+    // goes past them.  Adding the super-block in the lane offset also keeps
+    // the per-read offsets from being hoisted out of the loop into registers
+    // of their own.
+    const int rowsB = SB * kQ8_KBytes, wrowB = SB * kQ4_KBytes;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(X) + (int64_t)n0 * rowsB, (short)0, nrows * rowsB, kBufferWord3);
-    // codes: one instruction moves 4 rows (16 lanes per row, one chunk
-    // each); wave w's instruction i covers rows 4 (w + 4 i) .. +3, whose
-    // swizzle (row & 15) does not depend on i
-    const int crow = 4 * wave + (lane >> 4), cq = lane & 15;
-    const unsigned vo_codes = (unsigned)(crow * rowsB + 4 + 16 * (cq ^ (crow & 15)));
-    // sums and scales: wave w copies rows BN/4 w onward (32 rows of sums, 64
-    // scales), which covers its share of BN/4 rows
-    const unsigned vo_sums = (unsigned)((lane >> 1) * rowsB + 260 + 16 * (lane & 1));  // 32 rows x 2 halves
-    const unsigned vo_dx = (unsigned)(lane * rowsB);                                   // row l's scale
-    static_assert(BN / 4 <= 32 && BN / 4 * 3 + 64 <= BN + 48, "the sums and scales copies fit the tile");
-    // The row part of every copy's address is in the lane offset, which the
-    // descriptor's range check covers (the scalar offset, the super-block
-    // here, is not range-checked on gfx9-family chips), so rows at or past
-    // N read as zeros and no copy reaches past the workgroup's rows of X.
-    auto x_copy = [&](XTile<BN>& T, int sb) {
-        const unsigned sbB = (unsigned)(sb * kQ8_KBytes);
-        const int r0 = BN / 4 * wave;
-#pragma unroll
-        for (int i = 0; i < BN / 16; ++i)
-            copy16_to_lds(xr, &T.codes[4 * (wave + 4 * i)][0], vo_codes + (unsigned)(16 * i * rowsB), sbB);
-        copy16_to_lds(xr, &T.sums[r0][0], vo_sums + (unsigned)(r0 * rowsB), sbB);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, &T.dx[r0], 4, vo_dx + (unsigned)(r0 * rowsB), sbB, 0, 0);
+        const_cast<uint8_t*>(X) + (int64_t)n0 * rowsB, (short)0, min(BN, N - n0) * rowsB, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(Wt) + (int64_t)min(m0, M - 1) * wrowB, (short)0,
+        __builtin_amdgcn_readfirstlane(max(0, min(32, M - m0))) * wrowB, kBufferWord3);
+    // codes: 16-byte read i (of 8 TN per tile) holds tile rows 4i .. 4i+3
+    // (lane l: row 4i + l/16, position l%16 of the LDS row, which holds chunk
+    // (l%16) ^ (row & 15)); wave w takes reads w, w + W, ...  (read i's
+    // offset is that of read i%4 plus i/4 16-row groups, a scalar: with
+    // W >= 4 one vector register serves all of a wave's reads)
+    constexpr int CPW = 8 * TN / W;  // code reads per wave
+    static_assert(CPW * W == 8 * TN, "the code reads divide evenly among the waves");
+    auto vo_code = [&](const int i) {
+        const int row = 4 * (i & 3) + (lane >> 4);
+        return (unsigned)(row * rowsB + 4 + 16 * ((lane & 15) ^ row)) + (unsigned)((i >> 2) * 16 * rowsB);
     };
-    // ---- weights: header + this lane's halves of the four nibble-pair chunks
-    // two super-blocks of weights in flight (the next and the one after): one
-    // super-block of compute does not cover a load from HBM
-    uint4 wh, wq[4], wh2, wq2[4];
-    auto w_load = [&](int sb, uint4& hdr, uint4 (&q)[4]) {
-        sb = min(sb, sb1 - 1);  // past the end: a harmless repeat of the last super-block
-        const uint8_t* b = wrow + (int64_t)sb * kQ4_KBytes;
-        hdr = reinterpret_cast<const uint4*>(b)[0];
+    // weights: the wave's 32 rows of 144 bytes are 288 chunks of 16 bytes;
+    // read k holds chunks 64k .. 64k+63, stored to bytes 1024k + 16 lane of
+    // the wave's region (the last one's upper half repeats chunks 0-31 into
+    // the region's last 512 bytes, which nothing reads)
+    auto vo_w = [&](const int k) {
+        const int ch = (64 * k + lane) % 288;
+        return (unsigned)((ch / 9) * wrowB + 16 * (ch % 9));
+    };
+    // (weights into registers: read 0 is row c's header, read 1 + g its
+    // 16-byte half h of nibble-pair chunk g)
+    auto vo_wd = [&](const int k) { return (unsigned)(c * wrowB + (k ? 16 + 32 * (k - 1) + 16 * h : 0)); };
+    // sums: one read covers 32 rows (lane l: row l/2, half l%2); dx: one
+    // read covers 64 rows (4 bytes per lane).  Every wave issues the same
+    // number of reads (waves beyond the count repeat another wave's: the
+    // same bytes to the same place).
+    constexpr int SUMS_PW = TN >= W ? TN / W : 1, DX_PW = TN / 2 >= W ? TN / 2 / W : 1;
+    const unsigned vo_sums = (unsigned)((lane >> 1) * rowsB + 260 + 16 * (lane & 1));
+    const unsigned vo_dx = (unsigned)(lane * rowsB);
+    // The next super-block's operands are read into registers at the start
+    // of a step and stored to LDS at its end, so their latency is covered by
+    // the step's work (direct global-to-LDS copies would leave the compiler
+    // to order every LDS read after every copy still in flight).
+    u32x4 rc[CPW], rw[5], rs[SUMS_PW];
+    uint32_t rd[DX_PW];
+    auto fetch = [&](int sb) {
+        const unsigned so = (unsigned)(sb * kQ8_KBytes), wo = (unsigned)(sb * kQ4_KBytes);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) q[g] = reinterpret_cast<const uint4*>(b + 16 + 32 * g + 16 * h)[0];
+        for (int k = 0; k < CPW; ++k) rc[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, vo_code(wave + W * k) + so, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+            rw[k] = __builtin_amdgcn_raw_buffer_load_b128(wr, (kWLDS ? vo_w(k) : vo_wd(k)) + wo, 0, 0);
+#pragma unroll
+        for (int k = 0; k < SUMS_PW; ++k) {
+            const int g2 = (wave + W * k) % TN;  // 32-row group
+            rs[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, vo_sums + (unsigned)(32 * g2 * rowsB) + so, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < DX_PW; ++k) {
+            const int g4 = (wave + W * k) % (TN / 2);  // 64-row group
+            rd[k] = __builtin_amdgcn_raw_buffer_load_b32(xr, vo_dx + (unsigned)(64 * g4 * rowsB) + so, 0, 0);
+        }
+    };
+    auto store = [&](Q4KStage<TN, W, KS, kWLDS>& S, Q4KSums<TN, KS>& D) {
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) reinterpret_cast<u32x4*>(&S.codes[kp][4 * (wave + W * k)][0])[lane] = rc[k];
+#pragma unroll
+        for (int k = 0; k < (kWLDS ? 5 : 0); ++k) reinterpret_cast<u32x4*>(&S.w[kp][wave][64 * 16 * k])[lane] = rw[k];
+#pragma unroll
+        for (int k = 0; k < SUMS_PW; ++k) {
+            const int g2 = (wave + W * k) % TN;
+            reinterpret_cast<u32x4*>(&D.sums[kp][32 * g2][0])[lane] = rs[k];
+        }
+#pragma unroll
+        for (int k = 0; k < DX_PW; ++k) {
+            const int g4 = (wave + W * k) % (TN / 2);
+            D.dx[kp][64 * g4 + lane] = __uint_as_float(rd[k]);
+        }
     };
 
-    float yacc[NT][16];
+    float yacc[TN][16];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < TN; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
+    // With two tiles per wave there are registers for an accumulator per
+    // plane (kDual), which halves the activation operand reads from LDS.
+    constexpr bool kDual = TN == 2;
+    v16i acc[TN], acc_lo[kDual ? TN : 1];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[t] = (v16i){};
 
-    // one super-block: T is this super-block's tile, Tn receives the next one
-    auto step = [&](const int sb, XTile<BN>& T, XTile<BN>& Tn) {
-        const uint4 hdr = wh;
-        uint4 q[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) q[g] = wq[g];
-        wh = wh2;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) wq[g] = wq2[g];
-        // the activation copy goes first: loads retire in order, and the
-        // barrier that ends this super-block waits for the copy but not for
-        // the weights of super-block sb + 2 issued after it
-        if (sb + 1 < sb1) x_copy(Tn, sb + 1);
-        w_load(sb + 2, wh2, wq2);
+    // y[n][m] += dx_n * (d * sum_j sc_j P_j - dmin * sum_j m_j S_j) for the
+    // super-block with header hdr and sums and scales D
+    auto epilogue = [&](const uint4 hdr, const Q4KSums<TN, KS>& D) {
         const float d = h2f(hdr.x), dmin = h2f(hdr.x >> 16);
-        const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
-        const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
+        const uint32_t m03 = hdr.z & 0x3F3F3F3Fu;
         const uint32_t m47 = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
-
-        v16i ahi[NT], alo[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            ahi[t] = (v16i){};
-            alo[t] = (v16i){};
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint4 qq = q[j >> 1];
-            const int shift = (j & 1) * 4;
-            const uint32_t scw = (j < 4) ? sc03 : sc47;
-            const uint32_t sc = (scw >> (8 * (j & 3))) & 0xFF;
-            const uint32_t sh = sc >> 3, sl = sc & 7;
-            const uint32_t q0 = (qq.x >> shift) & 0x0F0F0F0Fu, q1 = (qq.y >> shift) & 0x0F0F0F0Fu;
-            const uint32_t q2 = (qq.z >> shift) & 0x0F0F0F0Fu, q3 = (qq.w >> shift) & 0x0F0F0F0Fu;
-            const v4i bh = {(int)mul_bytes(q0, sh), (int)mul_bytes(q1, sh), (int)mul_bytes(q2, sh),
-                            (int)mul_bytes(q3, sh)};
-            const v4i bl = {(int)mul_bytes(q0, sl), (int)mul_bytes(q1, sl), (int)mul_bytes(q2, sl),
-                            (int)mul_bytes(q3, sl)};
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const v4i a = *reinterpret_cast<const v4i*>(&T.codes[32 * t + c][16 * ((2 * j) ^ hsw)]);
-                ahi[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bh, ahi[t], 0, 0, 0);
-                alo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bl, alo[t], 0, 0, 0);
-            }
-        }
-        // min term (its tile is live only in the epilogue): lane K half h
-        // covers 16-wide sums 8h..8h+7, i.e. mins 4h..4h+3 twice each
+        // min term: A = the activation rows' 16-wide sums 8h .. 8h+7 (exact
+        // in fp16: |s| <= 2032), B = this lane's weight row's mins 4h .. 4h+3,
+        // each twice; products and their sum (< 2^24) are exact in fp32
         const uint32_t mw = h ? m47 : m03;
         v8h mins;
 #pragma unroll
         for (int e = 0; e < 8; ++e) mins[e] = (_Float16)(float)((mw >> (8 * (e >> 1))) & 0xFF);
-        // epilogue: y[n][m] += dx_n * (d * (8 P_hi + P_lo) - dmin * Smin)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const v8s bi = *reinterpret_cast<const v8s*>(&T.sums[32 * t + c][8 * h]);
-            v8h bs;  // int16 sums -> fp16 (exact: |s| <= 2032)
+        for (int t = 0; t < TN; ++t) {
+            const v8s bi = *reinterpret_cast<const v8s*>(&D.sums[kp][32 * t + c][8 * h]);
+            v8h bs;
 #pragma unroll
             for (int e = 0; e < 8; ++e) bs[e] = (_Float16)bi[e];
             const v16f amin = __builtin_amdgcn_mfma_f32_32x32x16_f16(bs, mins, (v16f){}, 0, 0, 0);
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const float4 dx = *reinterpret_cast<const float4*>(&T.dx[32 * t + 8 * qd + 4 * h]);
+                const float4 dx = *reinterpret_cast<const float4*>(&D.dx[kp][32 * t + 8 * qd + 4 * h]);
                 const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * qd + e;
-                    const int u = ahi[t][r] * 8 + alo[t][r];
-                    const float v = __builtin_fmaf((float)u, d, -(dmin * amin[r]));
+                    const float v = __builtin_fmaf((float)acc[t][r], d, -(dmin * amin[r]));
                     yacc[t][r] = __builtin_fmaf(v, dxa[e], yacc[t][r]);
                 }
             }
+            sched_fence();  // one tile's min-term result (16 registers) live at a time
         }
-        __syncthreads();  // the next tile has landed (waits for the copies) and this one is free
     };
 
-    w_load(sb0, wh, wq);
-    x_copy(tile0, sb0);
-    w_load(sb0 + 1, wh2, wq2);
-    __syncthreads();
-    // (each arm names its tiles statically, which is what lets the compiler
-    // tell the two apart)
-    for (int i = 0; i < SB / KS; ++i) {
-        if (i & 1) step(sb0 + i, tile1, tile0);
-        else step(sb0 + i, tile0, tile1);
-    }
+    const int hsw = c & 15;  // swizzle key of row 32t + c
 
-    if constexpr (KS == 2) {
-        // the second K part's sums, through LDS (the tiles are free: the
-        // last step issued no copy and ended with a barrier)
-        static_assert(sizeof(XTiles<BN, KS>) >= 4 * NT * 16 * 64 * sizeof(float), "partials fit a tile pair");
-        float* red = reinterpret_cast<float*>(&tiles0);
-        if (kh == 1) {
+    fetch(sb0);
+    store(st[0], sd[0]);
+    __syncthreads();
+    for (int i = 0; i < nsb; ++i) {
+        // super-block sb0 + i: its operands are in st[i % 2] and sd[i % 2];
+        // the next one's go to the other buffers
+        const int sb = sb0 + i, b2 = i & 1;
+        const Q4KStage<TN, W, KS, kWLDS>& S = st[b2];
+        // this lane's header and nibble-pair halves (row c, values 16h ..)
+        const uint8_t* wl = &S.w[kp][wave][kQ4_KBytes * c];
+        const uint4 hdr = kWLDS ? *reinterpret_cast<const uint4*>(wl) : __builtin_bit_cast(uint4, rw[0]);
+        uint4 q[4];
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+        for (int g = 0; g < 4; ++g)
+            q[g] = kWLDS ? *reinterpret_cast<const uint4*>(wl + 16 + 32 * g + 16 * h) : __builtin_bit_cast(uint4, rw[1 + g]);
+        const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu;
+        const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
+        auto operand = [&](const int j, const uint32_t s2) {
+            const uint4 qq = q[j >> 1];
+            const int sh = (j & 1) * 4;
+            return (v4i){mul_bytes2((qq.x >> sh) & 0x0F0F0F0Fu, s2), mul_bytes2((qq.y >> sh) & 0x0F0F0F0Fu, s2),
+                         mul_bytes2((qq.z >> sh) & 0x0F0F0F0Fu, s2), mul_bytes2((qq.w >> sh) & 0x0F0F0F0Fu, s2)};
+        };
+        auto act = [&](const int t, const int j) {
+            return *reinterpret_cast<const v4i*>(&S.codes[kp][32 * t + c][16 * ((2 * j + h) ^ hsw)]);
+        };
+        // One plane pass: per sub-block j, the weight operand (VALU), then TN
+        // matrix instructions, each followed by the LDS read of its
+        // activation operand for j + 1 into the register it has just read.
+        // A scheduling barrier after each sub-block keeps the compiler from
+        // hoisting every read (which would hold 32 TN registers), so the
+        // matrix core works through sub-block j while the wave builds the
+        // operand of j + 1 and the reads of j + 1 are in flight.
+        auto pass = [&](const uint32_t w03, const uint32_t w47, const bool first) {
+            v4i a[TN];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) red[((wave * NT + t) * 16 + r) * 64 + lane] = yacc[t][r];
+            for (int t = 0; t < TN; ++t) a[t] = act(t, 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // (the empty asm keeps the nibble extraction of a sub-block
+                // pair here instead of hoisted to the top of the step, where
+                // it would hold 32 registers)
+                if (!(j & 1)) opaque(q[j >> 1]);
+                const v4i b = operand(j, byte_u16x2(j < 4 ? w03 : w47, j & 3));
+#pragma unroll
+                for (int t = 0; t < TN; ++t) {
+                    acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], b, (first && j == 0) ? (v16i){} : acc[t],
+                                                                   0, 0, 0);
+                    if (j < 7) a[t] = act(t, j + 1);
+                }
+                sched_fence();
+            }
+        };
+        if constexpr (kDual) {
+            // both planes per sub-block, each activation operand read once
+            // for two matrix instructions: (sc >> 3) into acc, (sc & 7) into
+            // acc_lo; the epilogue forms 8 acc + acc_lo
+            fetch(min(sb + 1, sb0 + nsb - 1));
+            const uint32_t h03 = (sc03 >> 3) & 0x07070707u, h47 = (sc47 >> 3) & 0x07070707u;
+            const uint32_t l03 = sc03 & 0x07070707u, l47 = sc47 & 0x07070707u;
+            v4i a[TN];
+#pragma unroll
+            for (int t = 0; t < TN; ++t) a[t] = act(t, 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (!(j & 1)) opaque(q[j >> 1]);
+                const v4i bh = operand(j, byte_u16x2(j < 4 ? h03 : h47, j & 3));
+                const v4i bl = operand(j, byte_u16x2(j < 4 ? l03 : l47, j & 3));
+#pragma unroll
+                for (int t = 0; t < TN; ++t) {
+                    acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], bh, j ? acc[t] : (v16i){}, 0, 0, 0);
+                    acc_lo[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], bl, j ? acc_lo[t] : (v16i){}, 0, 0, 0);
+                    if (j < 7) a[t] = act(t, j + 1);
+                }
+                sched_fence();
+            }
+#pragma unroll
+            for (int t = 0; t < TN; ++t) acc[t] = (acc[t] << 3) + acc_lo[t];
+        } else {
+            pass((sc03 >> 3) & 0x07070707u, (sc47 >> 3) & 0x07070707u, true);   // (sc >> 3) plane
+            // the next super-block's operands, into registers (stored to the
+            // free buffers at the end of the step; the last step repeats its
+            // own).  Issued here rather than at the top, so that the registers
+            // they occupy are not live during the first pass.
+            fetch(min(sb + 1, sb0 + nsb - 1));
+#pragma unroll
+            for (int t = 0; t < TN; ++t) acc[t] = acc[t] << 3;
+            pass(sc03 & 0x07070707u, sc47 & 0x07070707u, false);                 // (sc & 7) plane
+        }
+
+        epilogue(hdr, sd[b2]);
+        store(st[b2 ^ 1], sd[b2 ^ 1]);
+        __syncthreads();  // the next operands are in place, and this step's buffers are free
+    }
+    if constexpr (KS > 1) {
+        // the K parts' partial sums, added in a fixed order through LDS (the
+        // stage buffers are free: the last step ended with a barrier that
+        // waited for its copy)
+        constexpr int kPart = W * TN * 16 * 64;  // floats of one K part
+        static_assert(sizeof(st[0]) >= (KS - 1) * kPart * sizeof(float), "partials fit a stage buffer");
+        float* red = reinterpret_cast<float*>(&st[0]);
+        if (kp > 0) {
+            float* dst = red + (kp - 1) * kPart;
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[((wave * TN + t) * 16 + r) * 64 + lane] = yacc[t][r];
         }
         __syncthreads();
-        if (kh == 1) return;
+        if (kp > 0) return;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int p = 1; p < KS; ++p)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) yacc[t][r] += red[((wave * NT + t) * 16 + r) * 64 + lane];
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) yacc[t][r] += red[(p - 1) * kPart + ((wave * TN + t) * 16 + r) * 64 + lane];
     }
 
     const int m = m0 + c;
     if (m < M) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < TN; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int n = n0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -989,6 +1113,17 @@ bool gemm_supported(int wtype) {
 constexpr int64_t kSplitKMaxTiles = 256;
 constexpr int kSplitQ32 = 2;  // K parts of the Q4_0 / Q5_0 / Q8_0 kernel on such grids
 
+// Q4_K kernel with TN tiles per wave, W waves per K part, KS K parts (SB %
+// KS == 0), WPE waves per SIMD.
+template <int TN, int W, int KS, int WPE>
+hipError_t launch_q4k(const uint8_t* w, const uint8_t* x, float* y, int64_t M, int64_t N, int SB, hipStream_t s) {
+    const int64_t mb = (M + 32 * W - 1) / (32 * W), nb = (N + 32 * TN - 1) / (32 * TN);
+    const int64_t groups = (mb * nb + 7) / 8;  // workgroups are dealt to the 8 XCDs in turn
+    if (groups * 8 * 64 * W * KS > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+    return launch(gemm_q4k_kernel<TN, W, KS, WPE>, dim3((unsigned)(8 * groups)), dim3(64 * W * KS), 0, s, w, x, y,
+                  (int)M, (int)N, SB, (int)mb, (int)nb);
+}
+
 hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
     if (!gemm_supported(wtype)) return hipErrorNotSupported;
@@ -1050,15 +1185,14 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
             return launch(gemm_narrow_q4k_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, s, w, x, y, (int)M,
                                (int)N, SB);
     }
-    // 64 activation rows per workgroup: two waves per SIMD fit (the 128-row
-    // tile needs one SIMD's registers per wave), measured faster at every size
-    const int64_t nb = (N + 63) / 64;
-    if (mblocks * nb <= kSplitKMaxTiles && SB % 2 == 0)  // K split in two: 8 waves per workgroup
-        return launch(gemm_q4k_kernel<2, 2>, grid(mblocks * nb), dim3(512), 0, s, w, x, y, (int)M, (int)N,
-                           SB, (int)mblocks, (int)nb);
-    else
-        return launch(gemm_q4k_kernel<2, 1>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N,
-                           SB, (int)mblocks, (int)nb);
+    // Grids of at least 192 workgroups of 256 weight rows x 128 activation
+    // rows: 8 waves of 4 tiles each, one workgroup per CU (LDS).  Smaller
+    // grids: 128 x 64 tiles with K split between two groups of 4 waves, or,
+    // with an odd count of super-blocks, 4-wave workgroups, two per CU.
+    const int64_t tiles_wide = ((M + 255) / 256) * ((N + 127) / 128);
+    if (tiles_wide >= 192) return launch_q4k<4, 8, 1, 2>(w, x, y, M, N, SB, s);
+    if (SB % 2 == 0) return launch_q4k<2, 4, 2, 2>(w, x, y, M, N, SB, s);
+    return launch_q4k<2, 4, 1, 2>(w, x, y, M, N, SB, s);
 }
 
 }  // namespace qmm
