@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
+PROBE_SINK_WORDS = 65536     # QMM_PROBE_SINK_WORDS (include/qmm_probe.h)
 METRIC = "GEMV effective GB/s (% HBM peak) at batch 1; GEMM int8 TOPS at batch 512"
 
 
@@ -55,9 +56,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--quick", action="store_true", help="headline only (no secondary workloads)")
-    p.add_argument("--only", metavar="PREFIX",
-                   help="run only the secondary workloads whose name starts with PREFIX (for profiling; "
-                        "prints their results, not the headline line)")
+    p.add_argument("--only", metavar="PREFIX[,PREFIX...]",
+                   help="run only the secondary workloads whose name starts with one of the prefixes (for "
+                        "profiling; prints their results, not the headline line)")
+    p.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                   help="summarise a `rocprofv3 --kernel-trace` CSV per kernel and launch shape (no GPU "
+                        "needed) and exit")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="summarise PMC counter runs (no GPU needed) and exit")
     return p.parse_args()
@@ -191,8 +195,10 @@ def decode_sweep(b: Bench, steps: int, warmup: int, keep_cpu_layers: int):
     sec = b.time_graph(g_fused, steps, warmup)
     g_unf = b.graph(step_unfused)
     sec_unf = b.time_graph(g_unf, steps, warmup)
+    launch_w_bytes = [sum(M * (K // 32) * 18 for (_, _, M) in mats) for _, K, mats in launches]
     return {
         "bytes_step": bytes_fused, "w_bytes": w_bytes, "seconds": sec, "steps": steps,
+        "launch_w_bytes": launch_w_bytes,
         "gbs": bytes_fused * steps / sec / 1e9, "ms_per_step": sec / steps * 1e3,
         "launches_per_step": len(launches),
         "unfused": {"gbs": round(bytes_unfused * steps / sec_unf / 1e9, 2),
@@ -201,8 +207,21 @@ def decode_sweep(b: Bench, steps: int, warmup: int, keep_cpu_layers: int):
     }, cpu_f32
 
 
-def cpu_baseline_decode(cpu_f32, min_seconds=10.0):
-    """The oracle (as it stands) on layers 0..L-1 of the same workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline_decode(cpu_f32, min_seconds=10.0, one_thread_seconds=5.0, gemm_seconds=5.0):
+    """The oracle (as it stands) on layers 0..L-1 of the same workload, with
+    all its threads and with one; and on a row sample of the Q4_K batch-512
+    prefill (int8 TOPS)."""
     import oracle as O
     import synth
     g = synth.rng(12345)
@@ -214,21 +233,50 @@ def cpu_baseline_decode(cpu_f32, min_seconds=10.0):
         per_rep_bytes += W.nbytes + (K // 32) * 34 + 4 * M
     per_rep_bytes += sum(4 * x.shape[1] + (x.shape[1] // 32) * 34 for x in xs)
     stage_of = {"attn_q": 0, "attn_k": 0, "attn_v": 0, "attn_output": 1, "ffn_gate": 2, "ffn_up": 2, "ffn_down": 3}
-    reps, t0 = 0, time.perf_counter()
+
+    def sweep(seconds):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            xq = [O.quantize(O.Q8_0, x) for x in xs]
+            for i, (name, W, M, K) in enumerate(mats):
+                li = i // 7
+                O.mul_mat(O.Q4_0, W, xq[4 * li + stage_of[name]], M, 1, K, with_T=False)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return reps, el
+
+    threads = O.num_threads()
+    reps, el = sweep(min_seconds)
+    O.set_num_threads(1)
+    try:
+        reps1, el1 = sweep(one_thread_seconds)
+    finally:
+        O.set_num_threads(threads)
+    # Q4_K prefill sample: 64 rows of a 4096x4096 Q4_K matrix against 512 activation rows
+    gm, gn, gk = 64, 512, 4096
+    Wk = synth.q4_k_random(g, gm, gk)
+    xk = O.quantize(O.Q8_K, synth.normal_f32(g, (gn, gk), 1.0))
+    greps, t0 = 0, time.perf_counter()
     while True:
-        xq = [O.quantize(O.Q8_0, x) for x in xs]
-        for i, (name, W, M, K) in enumerate(mats):
-            li = i // 7
-            O.mul_mat(O.Q4_0, W, xq[4 * li + stage_of[name]], M, 1, K, with_T=False)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
+        O.mul_mat(O.Q4_K, Wk, xk, gm, gn, gk, with_T=False)
+        greps += 1
+        gel = time.perf_counter() - t0
+        if gel >= gemm_seconds:
             break
-    return {"value": per_rep_bytes * reps / el / 1e9, "unit": "GB/s", "cores": O.num_threads(),
+    return {"value": per_rep_bytes * reps / el / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"layers 0-{len(layers) - 1} of the same 16-layer Q4_0 decode sweep "
                       f"({per_rep_bytes / 1e6:.1f} MB per pass), oracle quantize + fp64 product, "
-                      f"{reps} passes in {el:.1f} s"}
+                      f"{reps} passes in {el:.1f} s",
+            "cpu_model": cpu_model(),
+            "one_thread": {"value": per_rep_bytes * reps1 / el1 / 1e9, "unit": "GB/s",
+                           "sample": f"the same sample, {reps1} passes in {el1:.1f} s on 1 thread"},
+            "q4_k_gemm_batch512": {"value": 2 * gm * gn * gk * greps / gel / 1e12, "unit": "TOPS",
+                                   "cores": threads,
+                                   "sample": f"rows 0-{gm - 1} of a 4096x4096 Q4_K matrix x 512 Q8_K activation "
+                                             f"rows, {greps} passes in {gel:.1f} s"},
+            "note": "plain C fp64 correctness reference, not a tuned CPU kernel"}
 
 
 def copy_reference(b: Bench, nbytes=256 << 20, reps=10):
@@ -252,11 +300,81 @@ def copy_reference(b: Bench, nbytes=256 << 20, reps=10):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "gbs_read_plus_write": round(2 * nbytes * reps / sec / 1e9, 1)}
 
 
+def read_ceiling(b: Bench, nbytes=2 << 30, reps=3):
+    """The streaming-read ceiling: qmm_probe_read over a 2 GiB buffer (8x the
+    Infinity Cache), best of a few grid sizes."""
+    torch, Q = b.torch, b.Q
+    lib = Q.lib()
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=b.dev)
+    sink = torch.zeros(PROBE_SINK_WORDS, dtype=torch.int32, device=b.dev)
+    best = None
+    for groups in (0, 256, 512, 1024, 4096):
+        def run(groups=groups):
+            s = torch.cuda.current_stream().cuda_stream
+            for _ in range(4):
+                b.call(lib.qmm_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), groups, s), "probe read")
+        sec = b.time_graph(b.graph(run), reps, 1)
+        gbs = 4 * reps * nbytes / sec / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "workgroups": groups or min(2048, nbytes // 4096)}
+    del buf
+    torch.cuda.empty_cache()
+    best["bytes"] = nbytes
+    best["frac_hbm"] = round(best["gbs"] / HBM_PEAK_GBS, 4)
+    return best
+
+
+def mfma_ceiling(b: Bench, iters=20000, reps=3):
+    """The int8-MFMA ceiling: back-to-back v_mfma_i32_32x32x32_i8 on register
+    operands (qmm_probe_mfma), best of 1, 2 and 4 waves per SIMD."""
+    torch, Q = b.torch, b.Q
+    lib = Q.lib()
+    sink = torch.zeros(PROBE_SINK_WORDS, dtype=torch.int32, device=b.dev)
+    best = None
+    for groups in (256, 512, 1024):
+        def run(groups=groups):
+            s = torch.cuda.current_stream().cuda_stream
+            b.call(lib.qmm_probe_mfma(groups, iters, sink.data_ptr(), s), "probe mfma")
+        sec = b.time_graph(b.graph(run), reps, 1)
+        tops = reps * lib.qmm_probe_mfma_ops(groups, iters) / sec / 1e12
+        if best is None or tops > best["tops"]:
+            best = {"tops": round(tops, 1), "workgroups": groups, "waves_per_simd": groups * 4 // 1024}
+    best["frac_int8_peak"] = round(best["tops"] / INT8_PEAK_TOPS, 4)
+    return best
+
+
+def sweep_read_floor(b: Bench, launch_bytes, steps, warmup):
+    """qmm_probe_read in the decode sweep's launch structure: one launch per
+    stage, reading as many distinct weight bytes as that stage's matrices, 64
+    launches per step in one graph.  What a kernel that only streams the
+    weights achieves with this launch structure."""
+    torch, Q = b.torch, b.Q
+    lib = Q.lib()
+    total = sum(launch_bytes)
+    buf = torch.ones(total, dtype=torch.uint8, device=b.dev)
+    sink = torch.zeros(PROBE_SINK_WORDS, dtype=torch.int32, device=b.dev)
+    offs = np.concatenate([[0], np.cumsum(launch_bytes)[:-1]]).astype(np.int64)
+    assert all(n % 16 == 0 for n in launch_bytes)
+
+    def run():
+        s = torch.cuda.current_stream().cuda_stream
+        for o, n in zip(offs, launch_bytes):
+            b.call(lib.qmm_probe_read(buf.data_ptr() + int(o), int(n), sink.data_ptr(), 0, s), "probe read")
+    sec = b.time_graph(b.graph(run), steps, warmup)
+    del buf
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(sec / steps * 1e3, 4), "weight_gbs": round(total * steps / sec / 1e9, 1),
+            "launches_per_step": len(launch_bytes)}
+
+
 # ------------------------------------------------------- secondary loads
 
-def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=8):
-    """Per-launch time of one GEMV shape, rotating through copies of W so the
-    total exceeds the 256 MB Infinity Cache (every launch reads HBM)."""
+def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=8, read_floor=True):
+    """Per-launch time of one product shape, rotating through copies of W so
+    the total exceeds the 256 MB Infinity Cache (every launch reads HBM).
+    With read_floor, also the time qmm_probe_read takes to stream the same
+    weight bytes in the same launches: the floor a weight-streaming kernel
+    meets at this size and launch count."""
     import oracle as O
     import synth
     torch, Q = b.torch, b.Q
@@ -288,11 +406,24 @@ def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=
     sec = b.time_graph(gr, reps, 2)
     launches = reps * copies * rounds
     alg = wbytes + xq.numel() + 4 * N * M
+    out = {"us_per_launch": sec / launches * 1e6, "bytes_per_launch": alg,
+           "gbs": alg * launches / sec / 1e9, "frac_hbm": alg * launches / sec / 1e9 / HBM_PEAK_GBS,
+           "tops": 2 * M * N * K * launches / sec / 1e12, "copies": copies}
+    if read_floor and wbytes % 16 == 0:
+        # the same weight bytes, same rotation, read by qmm_probe_read alone
+        sink = torch.zeros(PROBE_SINK_WORDS, dtype=torch.int32, device=b.dev)
+
+        def run_read():
+            s = torch.cuda.current_stream().cuda_stream
+            for _ in range(rounds):
+                for w in Wg:
+                    lib.qmm_probe_read(w.data_ptr(), wbytes, sink.data_ptr(), 0, s)
+        rsec = b.time_graph(b.graph(run_read), reps, 2)
+        out["read_only_us"] = rsec / launches * 1e6
+        out["frac_of_read_only"] = rsec / sec
     del Wg
     torch.cuda.empty_cache()
-    return {"us_per_launch": sec / launches * 1e6, "bytes_per_launch": alg,
-            "gbs": alg * launches / sec / 1e9, "frac_hbm": alg * launches / sec / 1e9 / HBM_PEAK_GBS,
-            "tops": 2 * M * N * K * launches / sec / 1e12, "copies": copies}
+    return out
 
 
 def rotating_workload(b: Bench, launch, copies, bytes_per_launch, min_launches=8, reps=4):
@@ -397,11 +528,13 @@ def codec_workloads(b: Bench, want):
 
 
 def secondary(b: Bench, only=None):
-    """The other workloads; `only` keeps those whose name starts with it."""
+    """The other workloads; `only` (comma-separated prefixes) keeps those
+    whose name starts with one of them."""
     import oracle as O
     import synth
     out = {}
-    want = lambda name: only is None or name.startswith(only)
+    prefixes = None if only is None else tuple(p for p in only.split(",") if p)
+    want = lambda name: prefixes is None or name.startswith(prefixes)
     q80 = lambda g, M, K: O.quantize(O.Q8_0, synth.normal_f32(g, (M, K), 0.02))
     if want("q8_0_gemv_2048x2048_b1"):
         out["q8_0_gemv_2048x2048_b1"] = gemv_workload(b, b.Q.QMM_Q8_0, 2048, 2048, 1, q80)
@@ -419,15 +552,23 @@ def secondary(b: Bench, only=None):
             progress(f"q6_k head b{N} done")
     for M in (4096, 14336):
         if want(f"q4_k_gemm_{M}x4096_b512"):
-            r = gemv_workload(b, b.Q.QMM_Q4_K, M, 4096, 512, synth.q4_k_random, min_bytes=1, reps_floor=5)
+            r = gemv_workload(b, b.Q.QMM_Q4_K, M, 4096, 512, synth.q4_k_random, min_bytes=1, reps_floor=5,
+                              read_floor=False)
             r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
             out[f"q4_k_gemm_{M}x4096_b512"] = r
             progress(f"q4_k gemm {M}x4096 b512 {r['tops']:.1f} TOPS")
+    # Q6_K prefill: ffn_down of the 8B model (Q4_K_M keeps it at Q6_K)
+    if want("q6_k_gemm_4096x14336_b512"):
+        r = gemv_workload(b, b.Q.QMM_Q6_K, 4096, 14336, 512, synth.q6_k_random, min_bytes=1, reps_floor=5,
+                          read_floor=False)
+        r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
+        out["q6_k_gemm_4096x14336_b512"] = r
+        progress(f"q6_k gemm 4096x14336 b512 {r['tops']:.1f} TOPS")
     for name, wt, mk in (("q4_0", b.Q.QMM_Q4_0, lambda g, M, K: O.quantize(O.Q4_0, synth.normal_f32(g, (M, K), 0.02))),
                          ("q5_0", b.Q.QMM_Q5_0, synth.q5_0_random),
                          ("q8_0", b.Q.QMM_Q8_0, lambda g, M, K: O.quantize(O.Q8_0, synth.normal_f32(g, (M, K), 0.02)))):
         if want(f"{name}_gemm_4096x4096_b512"):
-            r = gemv_workload(b, wt, 4096, 4096, 512, mk, min_bytes=1, reps_floor=5)
+            r = gemv_workload(b, wt, 4096, 4096, 512, mk, min_bytes=1, reps_floor=5, read_floor=False)
             r["frac_int8_peak"] = r["tops"] / INT8_PEAK_TOPS
             out[f"{name}_gemm_4096x4096_b512"] = r
             progress(f"{name} gemm 4096x4096 b512 {r['tops']:.1f} TOPS")
@@ -510,10 +651,33 @@ def recorded_traffic():
     return rec["bytes_per_launch"], rec
 
 
+def trace_summary(path):
+    """Per (kernel, grid, workgroup) group of a rocprofv3 kernel trace: the
+    number of dispatches and their durations (End - Start), as markdown."""
+    import csv
+    import statistics
+    groups = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if name.startswith("void "):
+            name = name[5:]
+        name = name.replace("qmm::(anonymous namespace)::", "").split("(")[0]
+        key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("| kernel | grid (threads) | workgroup | dispatches | avg ns | median ns | min ns | max ns |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{name}` | {grid} | {wg} | {len(d)} | {statistics.fmean(d):.0f} | {statistics.median(d):.0f} | "
+              f"{min(d)} | {max(d)} |")
+
+
 def main():
     a = parse()
     if a.traffic:
         traffic_summary(*a.traffic)
+        return
+    if a.trace_summary:
+        trace_summary(a.trace_summary)
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the product shards by output "
@@ -529,6 +693,11 @@ def main():
     progress(f"copy reference {copy['gbs_read_plus_write']} GB/s")
     head, cpu_f32 = decode_sweep(b, a.steps, a.warmup, keep_cpu_layers=0 if a.no_cpu else 2)
     progress(f"decode sweep {head['gbs']:.1f} GB/s, {head['ms_per_step']:.4f} ms/step")
+    read = read_ceiling(b)
+    floor = sweep_read_floor(b, head["launch_w_bytes"], a.steps, a.warmup)
+    mfma = mfma_ceiling(b)
+    progress(f"ceilings: read {read['gbs']} GB/s, sweep read-only {floor['ms_per_step']} ms/step, "
+             f"int8 mfma {mfma['tops']} TOPS")
     gemv_us = head["seconds"] / (a.steps * head["launches_per_step"]) * 1e6
     traffic, rec = recorded_traffic()
     if traffic is not None:
@@ -572,11 +741,35 @@ def main():
             "traffic_note": traffic_note,
             "avg_launch_us": round(gemv_us, 3),
             "launches": head["launches_per_step"] * a.steps,
+            "measured_ceilings": {
+                "read_stream_gbs": read["gbs"],
+                "frac_of_read_stream": round(head["gbs"] / read["gbs"], 4),
+                "read_only_same_launches_ms_per_step": floor["ms_per_step"],
+                "frac_of_read_only_same_launches": round(floor["ms_per_step"] / head["ms_per_step"], 4),
+                "note": "read_stream: qmm_probe_read over 2 GiB; read_only_same_launches: qmm_probe_read "
+                        "streaming the same weight bytes in the same 64 graph launches per step (no "
+                        "activations, no arithmetic); frac_of_read_only_same_launches = its step time / "
+                        "this step time",
+            },
         },
         "copy_reference": copy,
+        "ceilings": {"read_stream": read, "decode_sweep_read_only": floor, "mfma_int8": mfma},
+        "context": {
+            "source": "page 'ggml', examples/gpt-2: sample performance on a MacBook M1 Pro CPU (whole-model "
+                      "decode, another machine and precision; not a target)",
+            "gpt2_ms_per_token_m1_pro": {"117M (240 MB)": 5, "345M (680 MB)": 12, "774M (1.5 GB)": 23,
+                                         "1558M (3.0 GB)": 42},
+            "same_bytes_at_this_decode_rate_ms": {
+                k: round(mb * 1e6 / (head["gbs"] * 1e9) * 1e3, 4)
+                for k, mb in (("117M (240 MB)", 240), ("345M (680 MB)", 680), ("774M (1.5 GB)", 1500),
+                              ("1558M (3.0 GB)", 3000))},
+        },
     }
     if not a.quick:
         sec = secondary(b)
+        for r in sec.values():
+            if "frac_int8_peak" in r:
+                r["frac_of_mfma_ceiling"] = r["tops"] / mfma["tops"]
         line["secondary"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                              for k, v in sec.items()}
         gm = [sec[k] for k in sec if k.startswith("q4_k_gemm")]

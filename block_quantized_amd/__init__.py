@@ -1,7 +1,8 @@
 """Python binding of libqmm, the gfx950 GGUF block-quantized matrix product.
 
 Argument marshalling only: every function named ``qmm_*`` forwards to the C
-function of the same name in ``libqmm.so`` (declared in ``include/qmm.h``).
+function of the same name in ``libqmm.so`` (declared in ``include/qmm.h`` and
+``include/qmm_probe.h``).
 Device buffers may be passed as torch tensors (their ``data_ptr()`` is used)
 or as integer device addresses; ``stream`` defaults to torch's current
 stream.  The ``qmm_*`` functions return the C status code.  The helpers
@@ -55,6 +56,9 @@ def lib() -> ctypes.CDLL:
             "qmm_mul_mat_algo": (I, [I, P, P, P, I64, I64, I64, I, P]),
             "qmm_mul_mat_multi": (I, [I, I, P, P, P, P, I, I64, I64, P]),
             "qmm_strerror": (ctypes.c_char_p, [I]),
+            "qmm_probe_read": (I, [P, I64, P, I, P]),
+            "qmm_probe_mfma": (I, [I, I64, P, P]),
+            "qmm_probe_mfma_ops": (I64, [I, I64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -65,7 +69,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("qmm_block_size", "qmm_block_bytes", "qmm_row_bytes", "qmm_vec_dot_type", "qmm_quantize_act",
             "qmm_quantize", "qmm_dequantize", "qmm_mul_mat", "qmm_mul_mat_algo", "qmm_mul_mat_multi",
-            "qmm_strerror")
+            "qmm_strerror", "qmm_probe_read", "qmm_probe_mfma", "qmm_probe_mfma_ops")
 
 
 def _ptr(a):
@@ -129,6 +133,18 @@ def qmm_mul_mat_multi(wtype, count, W, y, M, x, x_is_f32, N, K, stream=None) -> 
     ya = (ctypes.c_void_p * max(count, 1))(*[_ptr(t) for t in y[:count]]) if y is not None else None
     Ma = (ctypes.c_int64 * max(count, 1))(*M[:count]) if M is not None else None
     return lib().qmm_mul_mat_multi(wtype, count, Wa, ya, Ma, _ptr(x), int(bool(x_is_f32)), N, K, _stream(stream))
+
+
+def qmm_probe_read(src, nbytes, sink, workgroups=0, stream=None) -> int:
+    return lib().qmm_probe_read(_ptr(src), nbytes, _ptr(sink), workgroups, _stream(stream))
+
+
+def qmm_probe_mfma(workgroups, iters, sink, stream=None) -> int:
+    return lib().qmm_probe_mfma(workgroups, iters, _ptr(sink), _stream(stream))
+
+
+def qmm_probe_mfma_ops(workgroups, iters) -> int:
+    return lib().qmm_probe_mfma_ops(workgroups, iters)
 
 
 def qmm_strerror(code: int) -> str:

@@ -27,6 +27,7 @@ UNITS = {
     # MFMA results in VGPRs (not AGPRs): the epilogue reads them without
     # v_accvgpr_read, and register use drops enough for 2 waves per SIMD
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "probe.hip": [],
     "qmm.cpp": [],
 }
 

@@ -141,6 +141,25 @@ int qmm_mul_mat_multi(int wtype, int count, const void* const* W, float* const* 
                                         static_cast<hipStream_t>(stream)));
 }
 
+int qmm_probe_read(const void* src, int64_t bytes, uint32_t* sink, int workgroups, void* stream) {
+    if (!src || !sink) return QMM_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(src) & 15u) return QMM_ERR_ALIGN;
+    if (bytes <= 0 || bytes % 16 || workgroups < 0 || workgroups > QMM_PROBE_SINK_WORDS) return QMM_ERR_SHAPE;
+    const int64_t groups = workgroups ? workgroups : probe_read_groups(bytes);
+    return hip_status(launch_probe_read(src, bytes, sink, groups, static_cast<hipStream_t>(stream)));
+}
+
+int64_t qmm_probe_mfma_ops(int workgroups, int64_t iters) {
+    if (workgroups < 1 || workgroups > QMM_PROBE_SINK_WORDS || iters < 1 || iters > (int64_t(1) << 30)) return 0;
+    return probe_mfma_ops(workgroups, iters);
+}
+
+int qmm_probe_mfma(int workgroups, int64_t iters, uint32_t* sink, void* stream) {
+    if (!sink) return QMM_ERR_NULL;
+    if (qmm_probe_mfma_ops(workgroups, iters) == 0) return QMM_ERR_SHAPE;
+    return hip_status(launch_probe_mfma(workgroups, iters, sink, static_cast<hipStream_t>(stream)));
+}
+
 const char* qmm_strerror(int code) {
     switch (code) {
     case QMM_OK: return "ok";

@@ -9,6 +9,7 @@
 #include <type_traits>
 
 #include "../../include/qmm.h"
+#include "../../include/qmm_probe.h"
 
 namespace qmm {
 
@@ -87,5 +88,10 @@ bool gemv_fused_supported(int wtype, int64_t K);
 hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s);
 bool gemm_supported(int wtype);
+// Measurement kernels (qmm_probe.h).
+int64_t probe_read_groups(int64_t bytes);
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, int64_t groups, hipStream_t s);
+hipError_t launch_probe_mfma(int64_t groups, int64_t iters, uint32_t* sink, hipStream_t s);
+int64_t probe_mfma_ops(int64_t groups, int64_t iters);
 
 }  // namespace qmm

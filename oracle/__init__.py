@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
         L.orc_q6k_quant_n.argtypes = [P, I64, P]
         L.orc_q5_0_quant_n.argtypes = [P, I64, P]
         L.orc_num_threads.restype = I
+        L.orc_set_num_threads.argtypes = [I]
         _lib = L
     return _lib
 
@@ -194,3 +195,8 @@ def q5_0_quant_n(blocks: np.ndarray) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops (timing only; results do not depend on it)."""
+    lib().orc_set_num_threads(n)

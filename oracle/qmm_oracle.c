@@ -531,3 +531,13 @@ int orc_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads used by the parallel loops from now on (n >= 1); a timing control,
+ * no effect on any result. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

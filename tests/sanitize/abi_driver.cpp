@@ -12,6 +12,7 @@
 #include <initializer_list>
 
 #include "../../include/qmm.h"
+#include "../../include/qmm_probe.h"
 
 extern int g_launches;
 
@@ -132,6 +133,24 @@ int main() {
     const int64_t Mbad[2] = {64, 0};
     EXPECT(qmm_mul_mat_multi(QMM_Q4_K, 2, Ws, Ys, Mbad, X, 0, 1, 512, nullptr), QMM_ERR_SHAPE, 0);
     EXPECT(qmm_mul_mat_multi(QMM_Q8_K, 1, Ws, Ys, Ms, X, 0, 1, 512, nullptr), QMM_ERR_UNSUPPORTED, 0);
+
+    // ---- measurement aids
+    uint32_t* sink = reinterpret_cast<uint32_t*>(Y);
+    EXPECT(qmm_probe_read(A, 4096, sink, 0, nullptr), QMM_OK, 1);
+    EXPECT(qmm_probe_read(A, 64, sink, 3, nullptr), QMM_OK, 1);
+    EXPECT(qmm_probe_read(nullptr, 64, sink, 0, nullptr), QMM_ERR_NULL, 0);
+    EXPECT(qmm_probe_read(A, 64, nullptr, 0, nullptr), QMM_ERR_NULL, 0);
+    EXPECT(qmm_probe_read(mis, 64, sink, 0, nullptr), QMM_ERR_ALIGN, 0);
+    EXPECT(qmm_probe_read(A, 0, sink, 0, nullptr), QMM_ERR_SHAPE, 0);
+    EXPECT(qmm_probe_read(A, 40, sink, 0, nullptr), QMM_ERR_SHAPE, 0);
+    EXPECT(qmm_probe_read(A, 64, sink, -1, nullptr), QMM_ERR_SHAPE, 0);
+    EXPECT(qmm_probe_read(A, 64, sink, 65537, nullptr), QMM_ERR_SHAPE, 0);
+    EXPECT(qmm_probe_mfma(512, 100, sink, nullptr), QMM_OK, 1);
+    EXPECT(qmm_probe_mfma(512, 100, nullptr, nullptr), QMM_ERR_NULL, 0);
+    EXPECT(qmm_probe_mfma(0, 100, sink, nullptr), QMM_ERR_SHAPE, 0);
+    EXPECT(qmm_probe_mfma(512, 0, sink, nullptr), QMM_ERR_SHAPE, 0);
+    EXPECT(qmm_probe_mfma(512, (int64_t(1) << 30) + 1, sink, nullptr), QMM_ERR_SHAPE, 0);
+    if (qmm_probe_mfma_ops(2, 3) != 2LL * 16 * 3 * 65536 || qmm_probe_mfma_ops(65537, 1) != 0) ++failures;
 
     // ---- status text
     for (int c = -8; c <= 1; ++c)

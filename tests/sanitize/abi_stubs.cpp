@@ -30,4 +30,9 @@ bool gemm_supported(int wtype) {
     return wtype == QMM_Q4_K || wtype == QMM_Q6_K || wtype == QMM_Q4_0 || wtype == QMM_Q5_0 || wtype == QMM_Q8_0;
 }
 
+int64_t probe_read_groups(int64_t bytes) { return bytes / 4096 > 0 ? (bytes / 4096 < 2048 ? bytes / 4096 : 2048) : 1; }
+hipError_t launch_probe_read(const void*, int64_t, uint32_t*, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_probe_mfma(int64_t, int64_t, uint32_t*, hipStream_t) { ++g_launches; return hipSuccess; }
+int64_t probe_mfma_ops(int64_t groups, int64_t iters) { return groups * 16 * iters * 65536; }
+
 }  // namespace qmm

@@ -1,6 +1,7 @@
-"""The C-ABI library: it loads, exports every function include/qmm.h declares,
+"""The C-ABI library: it loads, exports every function include/*.h declares,
 and rejects invalid arguments before launching anything.  None of these calls
 reaches the GPU (validation returns first), so they run without one."""
+import glob
 import os
 import re
 
@@ -9,13 +10,15 @@ import pytest
 import block_quantized_amd as Q
 from conftest import ROOT
 
-HEADER = os.path.join(ROOT, "include", "qmm.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -125,3 +128,19 @@ def test_multi_errors_cpu(L):
     assert mm(Q.QMM_Q4_K, 1, [A], [A], [4], 0, 0, 1, 256, S) == Q.QMM_ERR_NULL
     assert mm(Q.QMM_Q4_K, 1, [A], [A], [4], A, 1, 9, 256, S) == Q.QMM_ERR_UNSUPPORTED
     assert mm(Q.QMM_Q4_0, 1, [A], [A], [4], A, 1, 1, 96, S) == Q.QMM_ERR_UNSUPPORTED
+
+
+def test_probe_errors_cpu(L):
+    assert Q.qmm_probe_read(0, 64, A, 0, S) == Q.QMM_ERR_NULL
+    assert Q.qmm_probe_read(A, 64, 0, 0, S) == Q.QMM_ERR_NULL
+    assert Q.qmm_probe_read(A + 4, 64, A, 0, S) == Q.QMM_ERR_ALIGN
+    assert Q.qmm_probe_read(A, 0, A, 0, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_read(A, 40, A, 0, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_read(A, 64, A, -1, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_read(A, 64, A, 65537, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_mfma(512, 10, 0, S) == Q.QMM_ERR_NULL
+    assert Q.qmm_probe_mfma(0, 10, A, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_mfma(512, 0, A, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_mfma(512, 2 ** 30 + 1, A, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_mfma_ops(2, 3) == 2 * 4 * 4 * 3 * 2 * 32 * 32 * 32
+    assert Q.qmm_probe_mfma_ops(0, 3) == 0

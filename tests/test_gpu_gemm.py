@@ -173,6 +173,21 @@ def test_gemm_q6k_head_sampled():
     assert_within_tolerance(y[:, rows], y_ref, T, what="Q6_K head N=32 (one row per 32-row tile)")
 
 
+def test_gemm_q6k_ffn_down_batch512():
+    # the 8B ffn_down (4096 x 14336, kept at Q6_K by Q4_K_M) at batch 512, as
+    # the benchmark runs it: every output written, one row of every 32-row
+    # tile against the oracle
+    g = np.random.default_rng(3)
+    M, K, N = 4096, 14336, 512
+    W = synth.q6_k_random(g, M, K)
+    xq = O.quantize(O.Q8_K, g.standard_normal((N, K), dtype=np.float32))
+    print("gemm q6_k ffn_down b512", flush=True)
+    y = run_product(Q.QMM_Q6_K, W, xq, M, N, K)
+    rows = tile_rows(M, seed=3)
+    y_ref, T = O.mul_mat(O.Q6_K, np.ascontiguousarray(W[rows]), xq, len(rows), N, K)
+    assert_within_tolerance(y[:, rows], y_ref, T, what="Q6_K 4096x14336 N=512 (one row per 32-row tile)")
+
+
 def test_gemm_q6k_deterministic_in_bounds_and_matches_gemv():
     g = np.random.default_rng(23)
     M, N, K = 700, 50, 2048

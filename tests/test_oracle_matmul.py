@@ -258,3 +258,22 @@ def test_zero_activation_gives_zero_output():
     X = O.quantize(O.Q8_K, np.zeros((2, 512), np.float32))
     y, T = O.mul_mat(O.Q4_K, W, X, 5, 2, 512)
     assert np.all(y == 0) and np.all(T == 0)
+
+
+def test_thread_count_does_not_change_results():
+    # the oracle parallelises over weight rows only: one thread and many give
+    # the same bits (timing control, no arithmetic effect)
+    g = np.random.default_rng(7)
+    M, N, K = 37, 3, 512
+    W = O.quantize(O.Q4_0, g.standard_normal((M, K), dtype=np.float32))
+    xq = O.quantize(O.Q8_0, g.standard_normal((N, K), dtype=np.float32))
+    n = O.num_threads()
+    y1, T1 = O.mul_mat(O.Q4_0, W, xq, M, N, K)
+    O.set_num_threads(1)
+    try:
+        y2, T2 = O.mul_mat(O.Q4_0, W, xq, M, N, K)
+    finally:
+        O.set_num_threads(n)
+    assert O.num_threads() == n
+    assert np.array_equal(y1.view(np.uint64), y2.view(np.uint64))
+    assert np.array_equal(T1.view(np.uint64), T2.view(np.uint64))
