@@ -36,9 +36,9 @@
 // v_mfma_i32_32x32x16_i8, one per sub-block: the weights enter as the int8
 // values q - 32 (in [-32, 31]), so no activation sums are needed, and since
 // sc_j * (q - 32) does not fit int8 the per-sub-block scale is applied to the
-// int32 tile by VALU (acc += sc_j * P_j, exact).  At the batch this serves
-// (the 32-row output head) the kernel is bound by streaming W, and those
-// VALU operations hide under the loads.
+// int32 tile by VALU (acc += sc_j * P_j, exact).  Up to 32 activation rows
+// (the output head) the product is bound by streaming W, and the weights go
+// through LDS so that they can be read in row-contiguous 16-byte pieces.
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -621,6 +621,201 @@ __global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict
     }
 }
 
+// Q6_K for up to 32 activation rows (the output head), with the weights
+// staged per wave through LDS.  gemm_q6k_kernel's lane-per-row 8-byte chunk
+// loads touch 32 rows per instruction and stream the 431 MB head at about
+// 4 TB/s (measured on MI355X).  Here a wave reads its tile of one super-block
+// (32 rows x the 192 bytes of ql and qh) with 16-byte loads that consecutive
+// lanes issue for consecutive pieces of a row (12 per row; about 5 TB/s for
+// the same head in a read-only probe), writes the tile to its own LDS region
+// after the current step's operands have been read from it, and each lane
+// then reads its 8-byte operand chunks (the same k assignment as
+// gemm_q6k_kernel) from there.  Scales and d are read per lane.  The 16
+// sub-blocks run in four groups that share a qh chunk, so a lane holds 6
+// operand registers at a time.  WPE waves per SIMD bound the registers.
+constexpr int kQ6WRow = 208;  // LDS bytes per weight row: ql|qh (192) + 16 (bank spread, 16-byte aligned)
+template <int NT, int WV, int WPE>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_q6k_lds_kernel(
+    const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, float* __restrict__ Y, int M, int N, int SB,
+    int mblk, int nblk) {
+    constexpr int BN = NT * 32;
+    constexpr int NTH = 64 * WV;
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][kCodeStride];
+    __shared__ __attribute__((aligned(16))) float s_dx[2][BN];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[WV][32 * kQ6WRow];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: bases in scalar registers
+    const int c = lane & 31, h = lane >> 5;
+    int rb, cb;
+    if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
+    const int m0 = rb * (32 * WV) + wave * 32;
+    const int n0 = cb * BN;
+    const int64_t rowB = (int64_t)SB * kQ6_KBytes;
+    const int last = M - 1 - m0;  // rows past M are computed on a copy of row M-1 and not stored
+    const uint8_t* wbase = W + (int64_t)min(m0, M - 1) * rowB;
+    // this lane's 6 pieces: piece g = 64 i + lane is row g / 12, bytes 16 (g % 12) .. +15
+    // (offsets recomputed where used: fewer registers held across the loop)
+    const int lastc = max(last, 0);
+    auto poff = [&](int i) {
+        const int g = 64 * i + lane, r = g / 12, pc = g - 12 * r;
+        return (uint32_t)(min(r, lastc) * (uint32_t)rowB + 16 * pc);
+    };
+    auto soff = [&](int i) {
+        const int g = 64 * i + lane, r = g / 12, pc = g - 12 * r;
+        return (uint32_t)(r * kQ6WRow + 16 * pc);
+    };
+    const uint32_t coff = (uint32_t)(min(c, max(last, 0)) * rowB);
+    uint8_t* const sw = s_w[wave];
+
+    // ---- activation staging: (row, piece) items of 16 codes; piece 0 also carries d
+    constexpr int ITEMS = BN * 16;
+    constexpr int IPT = (ITEMS + NTH - 1) / NTH;
+    u32x4_a4 xc[IPT];
+    uint32_t xd[IPT];
+    auto x_load = [&](int sb) {
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int it = (tid + NTH * k) % ITEMS;
+            const int rn = it >> 4, pc = it & 15;
+            const int n = min(n0 + rn, N - 1);
+            const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
+            xc[k] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 16 * pc);
+            xd[k] = *reinterpret_cast<const uint32_t*>(p);
+        }
+    };
+    auto x_store = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int it = tid + NTH * k;
+            if (it < ITEMS) {
+                const int rn = it >> 4, pc = it & 15;
+                *reinterpret_cast<uint4*>(&s_codes[buf][rn][16 * pc]) = make_uint4(xc[k].x, xc[k].y, xc[k].z, xc[k].w);
+                if (pc == 0) s_dx[buf][rn] = __uint_as_float(xd[k]);
+            }
+        }
+    };
+    u32x4_a2 wp[6];
+    u32x4_a2 scn;
+    uint32_t dn;
+    auto w_load = [&](int sb) {
+        const uint8_t* b = wbase + (int64_t)sb * kQ6_KBytes;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) wp[i] = *reinterpret_cast<const u32x4_a2*>(b + poff(i));
+        scn = *reinterpret_cast<const u32x4_a2*>(b + coff + 192);
+        dn = *reinterpret_cast<const uint16_t*>(b + coff + 208);
+    };
+    auto w_store = [&]() {
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            *reinterpret_cast<uint4*>(sw + soff(i)) = make_uint4(wp[i].x, wp[i].y, wp[i].z, wp[i].w);
+    };
+
+    float yacc[NT][16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
+
+    x_load(0);
+    w_load(0);
+    x_store(0);
+    w_store();
+    __syncthreads();
+
+    const uint8_t* const wrow_l = sw + c * kQ6WRow + 8 * h;
+    for (int sb = 0; sb < SB; ++sb) {
+        const int buf = sb & 1;
+        const u32x4_a2 sc4 = scn;
+        const uint32_t dcur = dn;
+        if (sb + 1 < SB) {
+            x_load(sb + 1);
+            w_load(sb + 1);
+        }
+        v16i acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = (v16i){};
+        auto product = [&](const int j, const int t, const long bq) {
+            const long a = *reinterpret_cast<const long*>(&s_codes[buf][32 * t + c][16 * j + 8 * h]);
+            return __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, (v16i){}, 0, 0, 0);
+        };
+        // sub-blocks in groups that share a qh chunk: group (h2, p) holds
+        // j = 8 h2 + 2 cc + p for cc = 0..3; ql chunks (h2, cc & 1, p)
+        v16i tl[2][NT];
+        int prev_sc = 0, have = 0;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int h2 = gq >> 1, p = gq & 1;
+            const u32x2 hq = *reinterpret_cast<const u32x2*>(wrow_l + 128 + 16 * (2 * h2 + p));
+            const u32x2 lq0 = *reinterpret_cast<const u32x2*>(wrow_l + 16 * (4 * h2 + p));
+            const u32x2 lq1 = *reinterpret_cast<const u32x2*>(wrow_l + 16 * (4 * h2 + 2 + p));
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int j = 8 * h2 + 2 * cc + p;
+                const u32x2 lq = (cc & 1) ? lq1 : lq0;
+                const int ls = (cc >> 1) * 4;
+                uint32_t b[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint32_t lo = (lq[e] >> ls) & 0x0F0F0F0Fu;
+                    const uint32_t hi = (hq[e] >> (2 * cc)) & 0x03030303u;
+                    b[e] = lo | __builtin_amdgcn_perm(0u, 0x1000F0E0u, hi);
+                }
+                long bq = (long)(((uint64_t)b[1] << 32) | b[0]);
+                if (have) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) order_after(bq, acc[t]);
+                }
+                const int cur = have & 1;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) tl[cur][t] = product(j, t, bq);
+                if (have) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[t][r] = __mul24(prev_sc, tl[cur ^ 1][t][r]) + acc[t][r];
+                }
+                prev_sc = (int)(int8_t)(sc4[j >> 2] >> (8 * (j & 3)));
+                ++have;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][r] = __mul24(prev_sc, tl[(have - 1) & 1][t][r]) + acc[t][r];
+        const float dw = h2f(dcur);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const float4 dx = *reinterpret_cast<const float4*>(&s_dx[buf][32 * t + 8 * qd + 4 * h]);
+                const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * qd + e;
+                    yacc[t][r] += (dw * dxa[e]) * (float)acc[t][r];
+                }
+            }
+        }
+        if (sb + 1 < SB) {
+            x_store(buf ^ 1);
+            w_store();
+        }
+        __syncthreads();
+    }
+
+    const int m = m0 + c;
+    if (m < M) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = n0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (n < N) Y[(int64_t)n * M + m] = yacc[t][r];
+            }
+    }
+}
+
 // ------------------------------------------------- Q4_0, Q5_0, Q8_0 weights
 // 32-value blocks with one fp16 scale each, against Q8_0 activations.  The
 // weight codes enter the MFMA as int8 (q - 8, q - 16 or q itself), one
@@ -1154,11 +1349,12 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         return go(gemm_q32_kernel<QMM_Q8_0, 1>, gemm_q32_kernel<QMM_Q8_0, kSplitQ32>);
     }
     if (wtype == QMM_Q6_K) {
-        // bound by streaming W: one 32-row activation tile per workgroup up to
-        // N = 32 (W read once), wider tiles beyond
+        // up to N = 32 (W read once) bound by streaming W: weights staged
+        // through LDS, 3 waves per SIMD; wider batches take 64-row activation
+        // tiles
         if (N <= 32) {
-            return launch(gemm_q6k_kernel<1>, grid(mblocks), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
-                               (int)mblocks, 1);
+            return launch(gemm_q6k_lds_kernel<1, 4, 3>, grid(mblocks), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
+                          (int)mblocks, 1);
         } else {
             const int64_t nb = (N + 63) / 64;
             return launch(gemm_q6k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
