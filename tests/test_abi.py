@@ -144,3 +144,11 @@ def test_probe_errors_cpu(L):
     assert Q.qmm_probe_mfma(512, 2 ** 30 + 1, A, S) == Q.QMM_ERR_SHAPE
     assert Q.qmm_probe_mfma_ops(2, 3) == 2 * 4 * 4 * 3 * 2 * 32 * 32 * 32
     assert Q.qmm_probe_mfma_ops(0, 3) == 0
+
+
+def test_launch_configuration_error_is_reported_cpu(L):
+    # Arguments that pass validation (M <= INT_MAX, every size fits) but whose
+    # GEMM grid would exceed 2^32 work-items: the launcher refuses before any
+    # HIP call and the status is QMM_ERR_HIP (no GPU needed, nothing enqueued).
+    assert Q.qmm_mul_mat_algo(Q.QMM_Q4_0, A, A, A, 2 ** 30, 512, 32, 2, S) == Q.QMM_ERR_HIP
+    assert Q.qmm_mul_mat(Q.QMM_Q8_0, A, A, A, 2 ** 30, 512, 32, S) == Q.QMM_ERR_HIP
