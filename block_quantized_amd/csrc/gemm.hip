@@ -450,189 +450,26 @@ void gemm_q4k_kernel(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__
 }
 
 // ------------------------------------------------------------------ Q6_K
-// Lane l = (c = l%32, h = l/32) feeds weight row m0 + c and, for sub-block j
-// (values 16j .. 16j+15 of the super-block), the 8 values 16j + 8h .. +7.
-// In the block those values' low 4 bits are 8 consecutive nibbles of ql and
-// their high 2 bits a 2-bit field of 8 consecutive qh bytes, so a lane reads
-// 8 ql chunks and 4 qh chunks of 8 bytes per super-block, plus the 16 scales
-// and d.  The activation operand holds the same 8 codes of the same
+// One v_mfma_i32_32x32x16_i8 per 16-value sub-block.  Lane l = (c = l%32,
+// h = l/32) feeds weight row m0 + c and, for sub-block j (values 16j .. 16j+15
+// of the super-block), the 8 values 16j + 8h .. +7; their low 4 bits are 8
+// consecutive nibbles of ql and their high 2 bits a 2-bit field of 8
+// consecutive qh bytes, so each lane's operand is an 8-byte ql chunk and an
+// 8-byte qh chunk.  The activation operand holds the same 8 codes of the same
 // sub-block (any consistent assignment of k to lanes gives the same sum).
-template <int NT>
-__global__ __launch_bounds__(256) void gemm_q6k_kernel(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int N, int SB,
-                                                       int mblk, int nblk) {
-    constexpr int BN = NT * 32;
-    __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BN][kCodeStride];
-    __shared__ __attribute__((aligned(16))) float s_dx[2][BN];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = lane & 31, h = lane >> 5;
-    int rb, cb;
-    if (!xcd_tile(nblk, mblk * nblk, rb, cb)) return;  // whole workgroup: no barrier is skipped
-    const int m0 = rb * 128 + wave * 32;
-    const int n0 = cb * BN;
-    const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
-    const uint8_t* wrow = W + (int64_t)mrow * SB * kQ6_KBytes;
-
-    // ---- activation staging: (row, quarter) items of 64 codes, plus d
-    constexpr int ITEMS = BN * 4;
-    constexpr int IPT = (ITEMS + 255) / 256;
-    u32x4_a4 xc[IPT][4];
-    uint32_t xd[IPT];
-    auto x_load = [&](int sb) {
-#pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int it = (tid + 256 * k) % ITEMS;  // unconditional, as for Q4_K
-            const int rn = it >> 2, qq = it & 3;
-            const int n = min(n0 + rn, N - 1);
-            const uint8_t* p = X + ((int64_t)n * SB + sb) * kQ8_KBytes;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) xc[k][d] = *reinterpret_cast<const u32x4_a4*>(p + 4 + 64 * qq + 16 * d);
-            xd[k] = *reinterpret_cast<const uint32_t*>(p);
-        }
-    };
-    auto x_store = [&](int buf) {
-#pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int it = tid + 256 * k;
-            if (it < ITEMS) {
-                const int rn = it >> 2, qq = it & 3;
-                uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][64 * qq]);
-#pragma unroll
-                for (int d = 0; d < 4; ++d) dst[d] = make_uint4(xc[k][d].x, xc[k][d].y, xc[k][d].z, xc[k][d].w);
-                if (qq == 0) s_dx[buf][rn] = __uint_as_float(xd[k]);
-            }
-        }
-    };
-    // ---- weights: ql chunk (h2, c&1, p) at 64 h2 + 32 (c&1) + 16 p + 8h;
-    //      qh chunk (h2, p) at 128 + 32 h2 + 16 p + 8h; scales; d
-    struct WQ {
-        u32x2_a2 ql[8], qh[4];
-        u32x4_a2 sc;
-        uint32_t d;
-    };
-    WQ wn;
-    auto w_load = [&](int sb, WQ& w) {
-        const uint8_t* b = wrow + (int64_t)sb * kQ6_KBytes + 8 * h;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w.ql[i] = *reinterpret_cast<const u32x2_a2*>(b + 16 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w.qh[i] = *reinterpret_cast<const u32x2_a2*>(b + 128 + 16 * i);
-        w.sc = *reinterpret_cast<const u32x4_a2*>(b - 8 * h + 192);
-        w.d = *reinterpret_cast<const uint16_t*>(b - 8 * h + 208);
-    };
-
-    float yacc[NT][16];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
-
-    x_load(0);
-    w_load(0, wn);
-    x_store(0);
-    __syncthreads();
-
-    for (int sb = 0; sb < SB; ++sb) {
-        const int buf = sb & 1;
-        const WQ w = wn;
-        if (sb + 1 < SB) {
-            x_load(sb + 1);
-            w_load(sb + 1, wn);
-        }
-        v16i acc[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = (v16i){};
-        // sub-block j's weight operand: the int8 values q - 32 of its 8 elements
-        auto operand = [&](const int j) {
-            const int h2 = j >> 3, cc = (j >> 1) & 3, p = j & 1;
-            const u32x2_a2 lq = w.ql[4 * h2 + 2 * (cc & 1) + p];
-            const u32x2_a2 hq = w.qh[2 * h2 + p];
-            const int ls = (cc >> 1) * 4;  // c < 2: low nibbles, else high
-            uint32_t b[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t lo = (lq[e] >> ls) & 0x0F0F0F0Fu;
-                const uint32_t hi = (hq[e] >> (2 * cc)) & 0x03030303u;
-                // byte (hi - 2) * 16 from a 4-entry byte table: E0 F0 00 10
-                b[e] = lo | __builtin_amdgcn_perm(0u, 0x1000F0E0u, hi);
-            }
-            return (long)(((uint64_t)b[1] << 32) | b[0]);
-        };
-        auto product = [&](const int j, const int t, const long bq) {
-            const long a = *reinterpret_cast<const long*>(&s_codes[buf][32 * t + c][16 * j + 8 * h]);
-            return __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, (v16i){}, 0, 0, 0);
-        };
-        // Software pipeline: the tile of sub-block j+1 is issued before the
-        // scale of sub-block j is applied, so the matrix core and the VALU
-        // overlap and at most two tiles per activation tile are live.  (The
-        // empty asm makes the operand of tile j+2 wait for the scaling of
-        // tile j; without it the compiler issues all 16 tiles first and
-        // holds them in 256 registers.)
-        v16i tl[2][NT];
-        {
-            const long bq = operand(0);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) tl[0][t] = product(0, t, bq);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            if (j + 1 < 16) {
-                long bq = operand(j + 1);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) order_after(bq, acc[t]);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) tl[(j + 1) & 1][t] = product(j + 1, t, bq);
-            }
-            const int sc = (int)(int8_t)(w.sc[j >> 2] >> (8 * (j & 3)));
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[t][r] = __mul24(sc, tl[j & 1][t][r]) + acc[t][r];  // |tile| < 2^17
-        }
-        // epilogue: y[n][m] += (d * dx_n) * sum_j sc_j * P_j   (the integer sum is exact)
-        const float dw = h2f(w.d);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const float4 dx = *reinterpret_cast<const float4*>(&s_dx[buf][32 * t + 8 * qd + 4 * h]);
-                const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * qd + e;
-                    yacc[t][r] += (dw * dxa[e]) * (float)acc[t][r];
-                }
-            }
-        }
-        if (sb + 1 < SB) x_store(buf ^ 1);
-        __syncthreads();
-    }
-
-    const int m = m0 + c;
-    if (m < M) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n = n0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (n < N) Y[(int64_t)n * M + m] = yacc[t][r];
-            }
-    }
-}
-
-// Q6_K for up to 32 activation rows (the output head), with the weights
-// staged per wave through LDS.  gemm_q6k_kernel's lane-per-row 8-byte chunk
-// loads touch 32 rows per instruction and stream the 431 MB head at about
-// 4 TB/s (measured on MI355X).  Here a wave reads its tile of one super-block
-// (32 rows x the 192 bytes of ql and qh) with 16-byte loads that consecutive
-// lanes issue for consecutive pieces of a row (12 per row; about 5 TB/s for
-// the same head in a read-only probe), writes the tile to its own LDS region
-// after the current step's operands have been read from it, and each lane
-// then reads its 8-byte operand chunks (the same k assignment as
-// gemm_q6k_kernel) from there.  Scales and d are read per lane.  The 16
-// sub-blocks run in four groups that share a qh chunk, so a lane holds 6
-// operand registers at a time.  WPE waves per SIMD bound the registers.
+//
+// The weights are staged per wave through LDS.  Lane-per-row 8-byte chunk
+// loads straight from memory touch 32 rows per instruction and streamed the
+// 431 MB output head at about 4 TB/s (measured on MI355X).  Here a wave reads
+// its tile of one super-block (32 rows x the 192 bytes of ql and qh) with
+// 16-byte loads that consecutive lanes issue for consecutive pieces of a row
+// (12 per row; about 5 TB/s for the same head in a read-only probe), writes
+// the tile to its own LDS region after the current step's operands have been
+// read from it, and each lane then reads its operand chunks from there.
+// Scales and d are read per lane.  The 16 sub-blocks run in four groups that
+// share a qh chunk, so a lane holds 6 operand registers at a time.  NT
+// activation tiles of 32 rows per wave, WV waves per workgroup, WPE waves per
+// SIMD (which bounds the registers).
 constexpr int kQ6WRow = 208;  // LDS bytes per weight row: ql|qh (192) + 16 (bank spread, 16-byte aligned)
 template <int NT, int WV, int WPE>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_q6k_lds_kernel(
@@ -1349,16 +1186,16 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         return go(gemm_q32_kernel<QMM_Q8_0, 1>, gemm_q32_kernel<QMM_Q8_0, kSplitQ32>);
     }
     if (wtype == QMM_Q6_K) {
-        // up to N = 32 (W read once) bound by streaming W: weights staged
-        // through LDS, 3 waves per SIMD; wider batches take 64-row activation
-        // tiles
+        // weights staged through LDS; up to N = 32 (W read once, bound by
+        // streaming W) 32-row activation tiles and 3 waves per SIMD, wider
+        // batches 64-row tiles (the registers of one wave per SIMD)
         if (N <= 32) {
             return launch(gemm_q6k_lds_kernel<1, 4, 3>, grid(mblocks), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
                           (int)mblocks, 1);
         } else {
             const int64_t nb = (N + 63) / 64;
-            return launch(gemm_q6k_kernel<2>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N, SB,
-                               (int)mblocks, (int)nb);
+            return launch(gemm_q6k_lds_kernel<2, 4, 1>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N,
+                          SB, (int)mblocks, (int)nb);
         }
     }
     if (N <= 16 && M <= 8192) {  // 16-row tiles: enough workgroups for every CU
