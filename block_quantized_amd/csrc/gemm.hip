@@ -895,9 +895,7 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow_q4k_kernel(cons
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, h = lane >> 5;
-    const int m0 = blockIdx.x * 32;
-    const int mrow = min(m0 + c, M - 1);  // rows past M are computed on a copy and not stored
-    const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
+    const int m0 = blockIdx.x * 32;  // rows past M are computed on a copy of row M-1 and not stored
     const int rowsB = SB * kQ8_KBytes;
     // activation rows past N read as zeros (their outputs are not stored)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(X), (short)0,
@@ -906,17 +904,29 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow_q4k_kernel(cons
     const int vo_sum = c * rowsB + 260 + 16 * h;  // sums 8h .. 8h+7 of row c
     const int vo_dx = c * rowsB;
 
+    // The wave's 32 rows x 144 bytes of a super-block are read as 288
+    // row-contiguous 16-byte pieces (consecutive lanes, consecutive pieces of a
+    // row) and written to the wave's own LDS region, piece g = 9 r + p at byte
+    // 16 g, where each lane then reads its row's header and nibble pairs.
+    // Lane-per-row 16-byte loads touch 32 rows per instruction and cost the
+    // texture path more: 13.7-14.3 us against 12.5-12.8 us at 14336x4096,
+    // N = 4 and 8 (measured on MI355X).
+    __shared__ __attribute__((aligned(16))) uint8_t s_wt[kNarrowWaves][5 * 64 * 16];
+    uint8_t* const swt = s_wt[wave];
+    const int64_t rowW = (int64_t)SB * kQ4_KBytes;
     struct Stage {
-        uint4 wh, wq[4];
+        u32x4 wp[5];
         u32x4 xa[8], bsum;
         uint32_t dx;
     };
     auto load = [&](Stage& st, int sb) {
         sb = min(sb, SB - 1);
-        const uint8_t* b = wrow + (int64_t)sb * kQ4_KBytes;
-        st.wh = reinterpret_cast<const uint4*>(b)[0];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) st.wq[g] = reinterpret_cast<const uint4*>(b + 16 + 32 * g + 16 * h)[0];
+        for (int i = 0; i < 5; ++i) {
+            const int g = min(64 * i + lane, 287), r = g / 9, pc = g - 9 * r;
+            st.wp[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)min(m0 + r, M - 1) * rowW +
+                                                        (int64_t)sb * kQ4_KBytes + 16 * pc);
+        }
         const int so = sb * kQ8_KBytes;
 #pragma unroll
         for (int j = 0; j < 8; ++j) st.xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, vo_code + 32 * j, so, 0);
@@ -929,7 +939,15 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow_q4k_kernel(cons
     for (int r = 0; r < 16; ++r) yacc[r] = 0.f;
 
     auto compute = [&](const Stage& st) {
-        const uint4 hdr = st.wh;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int g = 64 * i + lane;
+            if (g < 288) *reinterpret_cast<u32x4*>(swt + 16 * g) = st.wp[i];
+        }
+        const uint4 hdr = *reinterpret_cast<const uint4*>(swt + c * kQ4_KBytes);
+        uint4 wqv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) wqv[g] = *reinterpret_cast<const uint4*>(swt + c * kQ4_KBytes + 16 + 32 * g + 16 * h);
         const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
         const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
         const uint32_t m47 = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
@@ -940,7 +958,7 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow_q4k_kernel(cons
         v16i ahi = {}, alo = {};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint4 qq = st.wq[j >> 1];
+            const uint4 qq = wqv[j >> 1];
             const int shift = (j & 1) * 4;
             const uint32_t scw = (j < 4) ? sc03 : sc47;
             const uint32_t sc = (scw >> (8 * (j & 3))) & 0xFF;
@@ -1026,9 +1044,7 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow16_q4k_kernel(co
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, q = lane >> 4;
-    const int m0 = blockIdx.x * 16;
-    const int mrow = min(m0 + r, M - 1);  // rows past M are computed on a copy and not stored
-    const uint8_t* wrow = W + (int64_t)mrow * SB * kQ4_KBytes;
+    const int m0 = blockIdx.x * 16;  // rows past M are computed on a copy of row M-1 and not stored
     const int rowsB = SB * kQ8_KBytes;
     // activation rows past N read as zeros (their outputs are not stored)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(X), (short)0,
@@ -1039,17 +1055,24 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow16_q4k_kernel(co
     const int qsoff = 16 + 16 * (q & 1);         // this lane's 16 qs bytes of group g at + 32 g
     const int nsh = (q >> 1) * 4;                // low or high nibbles
 
+    // the wave's 16 rows x 144 bytes of a super-block, staged as in the
+    // 32-row kernel (144 pieces; 7.8 -> 5.9 us at 4096x4096, N = 8)
+    __shared__ __attribute__((aligned(16))) uint8_t s_wt[kNarrowWaves][3 * 64 * 16];
+    uint8_t* const swt = s_wt[wave];
+    const int64_t rowW = (int64_t)SB * kQ4_KBytes;
     struct Stage {
-        uint4 wh, wq[4];
+        u32x4 wp[3];
         u32x4 xa[4];
         uint32_t bsum[2], dx;
     };
     auto load = [&](Stage& st, int sb) {
         sb = min(sb, SB - 1);
-        const uint8_t* b = wrow + (int64_t)sb * kQ4_KBytes;
-        st.wh = reinterpret_cast<const uint4*>(b)[0];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) st.wq[g] = reinterpret_cast<const uint4*>(b + qsoff + 32 * g)[0];
+        for (int i = 0; i < 3; ++i) {
+            const int g = min(64 * i + lane, 143), rr = g / 9, pc = g - 9 * rr;
+            st.wp[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)min(m0 + rr, M - 1) * rowW +
+                                                        (int64_t)sb * kQ4_KBytes + 16 * pc);
+        }
         const int so = sb * kQ8_KBytes;
 #pragma unroll
         for (int g = 0; g < 4; ++g) st.xa[g] = __builtin_amdgcn_raw_buffer_load_b128(xr, vo_code + 64 * g, so, 0);
@@ -1062,7 +1085,15 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow16_q4k_kernel(co
     float yacc[4] = {0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const Stage& st) {
-        const uint4 hdr = st.wh;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int g = 64 * i + lane;
+            if (g < 144) *reinterpret_cast<u32x4*>(swt + 16 * g) = st.wp[i];
+        }
+        const uint4 hdr = *reinterpret_cast<const uint4*>(swt + r * kQ4_KBytes);
+        uint4 wqv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) wqv[g] = *reinterpret_cast<const uint4*>(swt + r * kQ4_KBytes + qsoff + 32 * g);
         const uint32_t sc03 = hdr.y & 0x3F3F3F3Fu, m03 = hdr.z & 0x3F3F3F3Fu;
         const uint32_t sc47 = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
         const uint32_t m47 = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
@@ -1073,7 +1104,7 @@ __global__ __launch_bounds__(64 * kNarrowWaves) void gemm_narrow16_q4k_kernel(co
         v4i ahi = {}, alo = {};
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const uint4 qq = st.wq[g];
+            const uint4 qq = wqv[g];
             const int j = 2 * g + (q >> 1);  // sub-block of this lane's 16 values
             const uint32_t scw = (g < 2) ? sc03 : sc47;
             const uint32_t sc = (scw >> (8 * (j & 3))) & 0xFF;

@@ -44,7 +44,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 int64_t gemm_min_rows(int wtype, int64_t M) {
     switch (wtype) {
     case QMM_Q6_K: return 8;
-    case QMM_Q4_K: return M > 256 * 32 ? 3 : 7;  // the narrow kernel's two-workgroups-per-CU form wins from N = 4
+    // the narrow MFMA kernels (weights staged through LDS) win from N = 2 on
+    // 16-row tiles (M <= 8192) and from N = 3 on 32-row tiles (4096- and
+    // 14336-row shapes); small matrices keep the GEMV longer
+    case QMM_Q4_K: return M > 256 * 32 ? 2 : M >= 2048 ? 1 : 7;
     // the Q4_0 / Q5_0 / Q8_0 GEMM takes about the same time for any N up
     // to 512 on these shapes, while the GEMV's grows with M N
     case QMM_Q4_0: return M > 8192 ? 24 : 48;
