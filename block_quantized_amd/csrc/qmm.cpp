@@ -43,7 +43,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 // and Q8_0 kernels' per-block scaling makes large.
 int64_t gemm_min_rows(int wtype, int64_t M) {
     switch (wtype) {
-    case QMM_Q6_K: return 8;
+    // the Q6_K GEMM has one 128-row workgroup per row block: below M = 8192
+    // too few to fill the chip (4096x14336: 114 us at any N <= 32, against
+    // 59-88 us for the GEMV at N = 9-16)
+    case QMM_Q6_K: return M > 256 * 32 ? 8 : 20;
     // the narrow MFMA kernels (weights staged through LDS) win from N = 2 on
     // 16-row tiles (M <= 8192) and from N = 3 on 32-row tiles (4096- and
     // 14336-row shapes); small matrices keep the GEMV longer
