@@ -674,11 +674,12 @@ struct Q32W<QMM_Q8_0> {
     }
     __device__ v4i operand(int) const { return (v4i){(int)q.x, (int)q.y, (int)q.z, (int)q.w}; }
 };
-// 4-bit codes (0..15) minus 8 as int8: (t ^ 8) is the 4-bit two's complement,
-// and bit 3 copied to bits 4-7 sign-extends it (0x08 * 0x1E = 0xF0, no carry)
+// 4-bit codes (0..15) minus 8 as int8, four per word: q + 0x78 stays below
+// 0x100 (no carry into the next byte), and flipping bit 7 of it leaves
+// q - 8 for q >= 8 and 0x100 + q - 8 for q < 8.  (Two full-rate operations;
+// a 32-bit multiply is a quarter-rate one.)
 __device__ __forceinline__ uint32_t nibbles_minus_8(uint32_t t) {
-    t ^= 0x08080808u;
-    return t | ((t & 0x08080808u) * 0x1Eu);
+    return (t + 0x78787878u) ^ 0x80808080u;
 }
 template <>
 struct Q32W<QMM_Q4_0> {
@@ -695,12 +696,15 @@ struct Q32W<QMM_Q4_0> {
                      (int)nibbles_minus_8((q.z >> sh) & 0x0F0F0F0Fu), (int)nibbles_minus_8((q.w >> sh) & 0x0F0F0F0Fu)};
     }
 };
-// 5-bit codes minus 16: bits 0-3 from the nibble, bit 4 from qh; as for Q4_0,
-// (q ^ 16) is the 5-bit two's complement, sign-extended from bit 4
+// 5-bit codes minus 16: bits 0-3 from the nibble, bit 4 from qh (bit k of
+// the 4 bits times 0x00204081 lands at bit 8k; a 24-bit multiply, full rate,
+// which the compiler does not pick by itself here); then as for Q4_0 with
+// q + 0x70, which stays below 0x100.
 __device__ __forceinline__ uint32_t q5_minus_16(uint32_t nib, uint32_t bits4) {
-    uint32_t t = nib | (((bits4 * 0x00204081u) & 0x01010101u) << 4);
-    t ^= 0x10101010u;
-    return t | ((t & 0x10101010u) * 0x0Eu);
+    uint32_t sp;
+    asm("v_mul_u32_u24_e32 %0, 0x204081, %1" : "=v"(sp) : "v"(bits4));
+    const uint32_t t = nib | ((sp & 0x01010101u) << 4);
+    return (t + 0x70707070u) ^ 0x80808080u;
 }
 template <>
 struct Q32W<QMM_Q5_0> {
@@ -783,16 +787,25 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
     uint8_t* const swc = s_wc_all[kh][wave];
     const int64_t rowWB = (int64_t)NB * Q32W<WT>::kBytes;
     u32x2 wpc[WC ? PW : 1];
+    // the wave's first row that exists (uniform) and each piece's 32-bit
+    // offset from it (rows past M read row M - 1; with K <= 65536 the offsets
+    // stay below 2^22)
+    const int wr0 = __builtin_amdgcn_readfirstlane(min(m0, M - 1));
+    const uint8_t* const wwave = W + (int64_t)wr0 * rowWB;
+    uint32_t woff[WC ? PW : 1];
+    if constexpr (WC) {
+#pragma unroll
+        for (int i = 0; i < PW; ++i) {
+            const int g = min(64 * i + lane, 32 * PR - 1), r = g / PR, pc = g - PR * r;
+            woff[i] = (uint32_t)(min(m0 + r, M - 1) - wr0) * (uint32_t)rowWB + 8 * pc;
+        }
+    }
     Q32W<WT> wn[WC ? 1 : CB];
     auto w_load = [&](int ch) {
         if constexpr (WC) {
-            ch = min(ch, NB / CB - 1);
+            const uint8_t* wb = wwave + (int64_t)min(ch, NB / CB - 1) * RBc;
 #pragma unroll
-            for (int i = 0; i < PW; ++i) {
-                const int g = min(64 * i + lane, 32 * PR - 1), r = g / PR, pc = g - PR * r;
-                wpc[i] = *reinterpret_cast<const u32x2*>(W + (int64_t)min(m0 + r, M - 1) * rowWB + (int64_t)ch * RBc +
-                                                         8 * pc);
-            }
+            for (int i = 0; i < PW; ++i) wpc[i] = *reinterpret_cast<const u32x2*>(wb + woff[i]);
         } else {
 #pragma unroll
             for (int j = 0; j < CB; ++j) wn[j].load(wrow + (int64_t)min(ch * CB + j, NB - 1) * Q32W<WT>::kBytes, h);
@@ -862,9 +875,14 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
             if (j < nb) {
                 const v4i bq = w[j].operand(h);
                 const float dw = h2f(w[j].d);
+                // both tiles' products are issued before either is scaled
+                v16i pp[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) pp[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[j & 1][t], bq, (v16i){}, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[j & 1][t], bq, (v16i){}, 0, 0, 0);
+                    const v16i p = pp[t];
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
                         const float4 dx = dxr[j & 1][t][qd];
