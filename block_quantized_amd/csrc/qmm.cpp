@@ -52,9 +52,11 @@ int64_t gemm_min_rows(int wtype, int64_t M) {
     // 14336-row shapes); small matrices keep the GEMV longer
     case QMM_Q4_K: return M > 256 * 32 ? 2 : M >= 2048 ? 1 : 7;
     // the Q4_0 / Q5_0 / Q8_0 GEMM takes about the same time for any N up
-    // to 512 on these shapes, while the GEMV's grows with M N
-    case QMM_Q4_0: return M > 8192 ? 24 : 48;
-    default: return M > 8192 ? 16 : 48;  // Q8_0, Q5_0
+    // to 512 on these shapes (4096 or 14336 rows, K = 4096: 44-60 us), while
+    // the GEMV's grows with M N; the switches are the measured crossovers
+    case QMM_Q4_0: return M > 8192 ? 18 : 36;
+    case QMM_Q8_0: return M > 8192 ? 12 : 32;
+    default: return M > 8192 ? 15 : 36;  // Q5_0
     }
 }
 

@@ -145,8 +145,8 @@ int qmm_dequantize(int type, const void* blocks, float* out, int64_t rows, int64
  * MI355X: for Q6_K N > 8 when M > 8192, else N > 20; for Q4_K N > 1 when
  * 2048 <= M <= 8192, N > 2 when M > 8192, else N > 7 (Q4_K with N <= 32
  * takes narrow MFMA kernels, on 32- or 16-row tiles, that split K over the
- * waves of a workgroup); for Q4_0, Q8_0 and Q5_0, N > 48, or N > 24 (Q4_0)
- * and N > 16 (Q8_0, Q5_0) when M > 8192. */
+ * waves of a workgroup); for Q4_0, Q8_0 and Q5_0, N > 36 / 32 / 36, or
+ * N > 18 / 12 / 15 when M > 8192. */
 int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y,
                 int64_t M, int64_t N, int64_t K, void* stream);
 
