@@ -324,23 +324,39 @@ def read_ceiling(b: Bench, nbytes=2 << 30, reps=3):
     return best
 
 
+def device_facts(b: Bench):
+    """What the runtime reports for the device the ceilings were measured on
+    (the vendor peaks assume 256 compute units at 2.4 GHz)."""
+    p = b.torch.cuda.get_device_properties(b.dev)
+    return {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2 ** 30, 1), "l2_bytes": p.L2_cache_size}
+
+
 def mfma_ceiling(b: Bench, iters=20000, reps=3):
-    """The int8-MFMA ceiling: back-to-back v_mfma_i32_32x32x32_i8 on register
-    operands (qmm_probe_mfma), best of 1, 2 and 4 waves per SIMD."""
+    """The int8-MFMA ceiling: back-to-back int8 MFMAs on register operands,
+    best of 1, 2 and 4 waves per SIMD, for the two instruction forms the
+    kernels use: v_mfma_i32_32x32x32_i8 (qmm_probe_mfma) and
+    v_mfma_i32_16x16x64_i8 (qmm_probe_mfma16).  `tops` is the better form."""
     torch, Q = b.torch, b.Q
     lib = Q.lib()
     sink = torch.zeros(PROBE_SINK_WORDS, dtype=torch.int32, device=b.dev)
-    best = None
-    for groups in (256, 512, 1024):
-        def run(groups=groups):
-            s = torch.cuda.current_stream().cuda_stream
-            b.call(lib.qmm_probe_mfma(groups, iters, sink.data_ptr(), s), "probe mfma")
-        sec = b.time_graph(b.graph(run), reps, 1)
-        tops = reps * lib.qmm_probe_mfma_ops(groups, iters) / sec / 1e12
-        if best is None or tops > best["tops"]:
-            best = {"tops": round(tops, 1), "workgroups": groups, "waves_per_simd": groups * 4 // 1024}
-    best["frac_int8_peak"] = round(best["tops"] / INT8_PEAK_TOPS, 4)
-    return best
+    forms = {"32x32x32": (lib.qmm_probe_mfma, lib.qmm_probe_mfma_ops),
+             "16x16x64": (lib.qmm_probe_mfma16, lib.qmm_probe_mfma16_ops)}
+    out = {}
+    for form, (probe, ops) in forms.items():
+        best = None
+        for groups in (256, 512, 1024):
+            def run(groups=groups, probe=probe):
+                s = torch.cuda.current_stream().cuda_stream
+                b.call(probe(groups, iters, sink.data_ptr(), s), "probe mfma " + form)
+            sec = b.time_graph(b.graph(run), reps, 1)
+            tops = reps * ops(groups, iters) / sec / 1e12
+            if best is None or tops > best["tops"]:
+                best = {"tops": round(tops, 1), "workgroups": groups, "waves_per_simd": groups * 4 // 1024}
+        best["frac_int8_peak"] = round(best["tops"] / INT8_PEAK_TOPS, 4)
+        out[form] = best
+    top = max(out, key=lambda f: out[f]["tops"])
+    return dict(out[top], form=top, forms=out)
 
 
 def sweep_read_floor(b: Bench, launch_bytes, steps, warmup):
@@ -754,6 +770,7 @@ def main():
         },
         "copy_reference": copy,
         "ceilings": {"read_stream": read, "decode_sweep_read_only": floor, "mfma_int8": mfma},
+        "device": device_facts(b),
         "context": {
             "source": "page 'ggml', examples/gpt-2: sample performance on a MacBook M1 Pro CPU (whole-model "
                       "decode, another machine and precision; not a target)",

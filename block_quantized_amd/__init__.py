@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
             "qmm_probe_read": (I, [P, I64, P, I, P]),
             "qmm_probe_mfma": (I, [I, I64, P, P]),
             "qmm_probe_mfma_ops": (I64, [I, I64]),
+            "qmm_probe_mfma16": (I, [I, I64, P, P]),
+            "qmm_probe_mfma16_ops": (I64, [I, I64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -69,7 +71,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("qmm_block_size", "qmm_block_bytes", "qmm_row_bytes", "qmm_vec_dot_type", "qmm_quantize_act",
             "qmm_quantize", "qmm_dequantize", "qmm_mul_mat", "qmm_mul_mat_algo", "qmm_mul_mat_multi",
-            "qmm_strerror", "qmm_probe_read", "qmm_probe_mfma", "qmm_probe_mfma_ops")
+            "qmm_strerror", "qmm_probe_read", "qmm_probe_mfma", "qmm_probe_mfma_ops",
+            "qmm_probe_mfma16", "qmm_probe_mfma16_ops")
 
 
 def _ptr(a):
@@ -145,6 +148,14 @@ def qmm_probe_mfma(workgroups, iters, sink, stream=None) -> int:
 
 def qmm_probe_mfma_ops(workgroups, iters) -> int:
     return lib().qmm_probe_mfma_ops(workgroups, iters)
+
+
+def qmm_probe_mfma16(workgroups, iters, sink, stream=None) -> int:
+    return lib().qmm_probe_mfma16(workgroups, iters, _ptr(sink), _stream(stream))
+
+
+def qmm_probe_mfma16_ops(workgroups, iters) -> int:
+    return lib().qmm_probe_mfma16_ops(workgroups, iters)
 
 
 def qmm_strerror(code: int) -> str:

@@ -18,6 +18,7 @@ constexpr int kReadUnroll = 8;
 constexpr int kReadMaxGroups = 2048;  // 8 workgroups of 4 waves per compute unit
 constexpr int kMfmaThreads = 256;
 constexpr int kMfmaChains = 4;        // independent accumulators per wave
+constexpr int kMfma16Chains = 8;      // the same for the 16x16x64 form (shorter latency per instruction)
 
 __device__ __forceinline__ uint32_t wave_xor(uint32_t x) {
     for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
@@ -54,6 +55,27 @@ __global__ __launch_bounds__(kReadThreads) void read_kernel(const u32x4* __restr
     }
     for (; i < n16; i += stride) acc ^= src[i];
     store_group_xor(acc.x ^ acc.y ^ acc.z ^ acc.w, sink);
+}
+
+// The same for v_mfma_i32_16x16x64_i8 (16x16 tiles over K = 64: the form
+// the 16-row narrow kernels use), kMfma16Chains accumulators per wave.
+__global__ __launch_bounds__(kMfmaThreads) void mfma16_kernel(int64_t iters, uint32_t* sink) {
+    const int l = (int)threadIdx.x;
+    const v4i a = {l * 0x01030507, l ^ 0x0f0e0d0c, l * 0x11, l + 0x7f7f7f7f};
+    const v4i b = {l * 0x02040608, l ^ 0x70605040, l * 0x13, l - 0x01010101};
+    v4i acc[kMfma16Chains];
+#pragma unroll
+    for (int c = 0; c < kMfma16Chains; ++c) acc[c] = (v4i){};
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < kMfma16Chains; ++c) acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[c], 0, 0, 0);
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int c = 0; c < kMfma16Chains; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x ^= (uint32_t)acc[c][e] * (uint32_t)(2 * (c * 4 + e) + 1);
+    store_group_xor(x, sink);
 }
 
 // kMfmaChains independent v_mfma_i32_32x32x32_i8 accumulations per wave,
@@ -97,6 +119,14 @@ hipError_t launch_probe_mfma(int64_t groups, int64_t iters, uint32_t* sink, hipS
 
 int64_t probe_mfma_ops(int64_t groups, int64_t iters) {
     return groups * (kMfmaThreads / 64) * kMfmaChains * iters * (int64_t)(2 * 32 * 32 * 32);
+}
+
+hipError_t launch_probe_mfma16(int64_t groups, int64_t iters, uint32_t* sink, hipStream_t s) {
+    return launch(mfma16_kernel, dim3((unsigned)groups), dim3(kMfmaThreads), 0, s, iters, sink);
+}
+
+int64_t probe_mfma16_ops(int64_t groups, int64_t iters) {
+    return groups * (kMfmaThreads / 64) * kMfma16Chains * iters * (int64_t)(2 * 16 * 16 * 64);
 }
 
 }  // namespace qmm

@@ -168,6 +168,17 @@ int qmm_probe_mfma(int workgroups, int64_t iters, uint32_t* sink, void* stream) 
     return hip_status(launch_probe_mfma(workgroups, iters, sink, static_cast<hipStream_t>(stream)));
 }
 
+int64_t qmm_probe_mfma16_ops(int workgroups, int64_t iters) {
+    if (workgroups < 1 || workgroups > QMM_PROBE_SINK_WORDS || iters < 1 || iters > (int64_t(1) << 30)) return 0;
+    return probe_mfma16_ops(workgroups, iters);
+}
+
+int qmm_probe_mfma16(int workgroups, int64_t iters, uint32_t* sink, void* stream) {
+    if (!sink) return QMM_ERR_NULL;
+    if (qmm_probe_mfma16_ops(workgroups, iters) == 0) return QMM_ERR_SHAPE;
+    return hip_status(launch_probe_mfma16(workgroups, iters, sink, static_cast<hipStream_t>(stream)));
+}
+
 const char* qmm_strerror(int code) {
     switch (code) {
     case QMM_OK: return "ok";

@@ -93,5 +93,7 @@ int64_t probe_read_groups(int64_t bytes);
 hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, int64_t groups, hipStream_t s);
 hipError_t launch_probe_mfma(int64_t groups, int64_t iters, uint32_t* sink, hipStream_t s);
 int64_t probe_mfma_ops(int64_t groups, int64_t iters);
+hipError_t launch_probe_mfma16(int64_t groups, int64_t iters, uint32_t* sink, hipStream_t s);
+int64_t probe_mfma16_ops(int64_t groups, int64_t iters);
 
 }  // namespace qmm

@@ -55,6 +55,18 @@ int qmm_probe_mfma(int workgroups, int64_t iters, uint32_t* sink, void* stream);
  * arguments it would reject. */
 int64_t qmm_probe_mfma_ops(int workgroups, int64_t iters);
 
+/* As qmm_probe_mfma, with v_mfma_i32_16x16x64_i8 (16x16 tiles, K = 64) and 8
+ * independent accumulator chains per wave.  Integer operations performed:
+ * qmm_probe_mfma16_ops(workgroups, iters) = workgroups * 4 * 8 * iters * 32768.
+ *   workgroups : 1..QMM_PROBE_SINK_WORDS;  iters : 1..2^30
+ *   (QMM_ERR_SHAPE otherwise)
+ * Returns QMM_OK, QMM_ERR_NULL, QMM_ERR_SHAPE or QMM_ERR_HIP. */
+int qmm_probe_mfma16(int workgroups, int64_t iters, uint32_t* sink, void* stream);
+
+/* Integer operations of one qmm_probe_mfma16 call; 0 for arguments it would
+ * reject. */
+int64_t qmm_probe_mfma16_ops(int workgroups, int64_t iters);
+
 #ifdef __cplusplus
 }
 #endif

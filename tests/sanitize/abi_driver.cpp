@@ -151,6 +151,11 @@ int main() {
     EXPECT(qmm_probe_mfma(512, 0, sink, nullptr), QMM_ERR_SHAPE, 0);
     EXPECT(qmm_probe_mfma(512, (int64_t(1) << 30) + 1, sink, nullptr), QMM_ERR_SHAPE, 0);
     if (qmm_probe_mfma_ops(2, 3) != 2LL * 16 * 3 * 65536 || qmm_probe_mfma_ops(65537, 1) != 0) ++failures;
+    EXPECT(qmm_probe_mfma16(512, 100, sink, nullptr), QMM_OK, 1);
+    EXPECT(qmm_probe_mfma16(512, 100, nullptr, nullptr), QMM_ERR_NULL, 0);
+    EXPECT(qmm_probe_mfma16(0, 100, sink, nullptr), QMM_ERR_SHAPE, 0);
+    EXPECT(qmm_probe_mfma16(512, 0, sink, nullptr), QMM_ERR_SHAPE, 0);
+    if (qmm_probe_mfma16_ops(2, 3) != 2LL * 32 * 3 * 32768 || qmm_probe_mfma16_ops(65537, 1) != 0) ++failures;
 
     // ---- status text
     for (int c = -8; c <= 1; ++c)

@@ -34,5 +34,7 @@ int64_t probe_read_groups(int64_t bytes) { return bytes / 4096 > 0 ? (bytes / 40
 hipError_t launch_probe_read(const void*, int64_t, uint32_t*, int64_t, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_probe_mfma(int64_t, int64_t, uint32_t*, hipStream_t) { ++g_launches; return hipSuccess; }
 int64_t probe_mfma_ops(int64_t groups, int64_t iters) { return groups * 16 * iters * 65536; }
+hipError_t launch_probe_mfma16(int64_t, int64_t, uint32_t*, hipStream_t) { ++g_launches; return hipSuccess; }
+int64_t probe_mfma16_ops(int64_t groups, int64_t iters) { return groups * 32 * iters * 32768; }
 
 }  // namespace qmm

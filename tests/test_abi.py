@@ -144,6 +144,13 @@ def test_probe_errors_cpu(L):
     assert Q.qmm_probe_mfma(512, 2 ** 30 + 1, A, S) == Q.QMM_ERR_SHAPE
     assert Q.qmm_probe_mfma_ops(2, 3) == 2 * 4 * 4 * 3 * 2 * 32 * 32 * 32
     assert Q.qmm_probe_mfma_ops(0, 3) == 0
+    assert Q.qmm_probe_mfma16(512, 10, 0, S) == Q.QMM_ERR_NULL
+    assert Q.qmm_probe_mfma16(0, 10, A, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_mfma16(65537, 10, A, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_mfma16(512, 0, A, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_mfma16(512, 2 ** 30 + 1, A, S) == Q.QMM_ERR_SHAPE
+    assert Q.qmm_probe_mfma16_ops(2, 3) == 2 * 4 * 8 * 3 * 2 * 16 * 16 * 64
+    assert Q.qmm_probe_mfma16_ops(2, 0) == 0
 
 
 def test_launch_configuration_error_is_reported_cpu(L):

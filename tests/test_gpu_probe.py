@@ -37,11 +37,13 @@ def test_read_checksum(nbytes, groups):
     assert np.all(got[used:] == 0xFFFFFFFF), "wrote past its workgroups' words"
 
 
-def test_mfma_deterministic():
-    say("probe mfma")
+@pytest.mark.parametrize("form", ["32x32x32", "16x16x64"])
+def test_mfma_deterministic(form):
+    say("probe mfma", form)
+    run = Q.qmm_probe_mfma if form == "32x32x32" else Q.qmm_probe_mfma16
     sinks = [torch.full((WORDS,), -1, dtype=torch.int32, device="cuda") for _ in range(2)]
     for s in sinks:
-        assert Q.qmm_probe_mfma(64, 100, s) == Q.QMM_OK
+        assert run(64, 100, s) == Q.QMM_OK
     a, b = (to_cpu(s).view(np.uint32) for s in sinks)
     assert np.array_equal(a, b)
     assert np.all(a[64:] == 0xFFFFFFFF)
