@@ -385,6 +385,17 @@ def sweep_read_floor(b: Bench, launch_bytes, steps, warmup):
 
 # ------------------------------------------------------- secondary loads
 
+def kernel_family(Q, wtype, M, N, K):
+    """The kernels qmm_mul_mat runs for this shape (its automatic choice, as
+    the library reports it; the row names keep the workload they stand for)."""
+    choice = Q.qmm_mul_mat_choice(wtype, M, N, K)
+    if choice == 1:
+        return "gemv (VALU dot4)"
+    if choice == 2:
+        return "int8 MFMA, narrow (K split over waves)" if wtype == Q.QMM_Q4_K and N <= 32 else "int8 MFMA GEMM"
+    raise ValueError(f"shape rejected: type {wtype} {M}x{K} N={N}")
+
+
 def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=8, read_floor=True):
     """Per-launch time of one product shape, rotating through copies of W so
     the total exceeds the 256 MB Infinity Cache (every launch reads HBM).
@@ -424,7 +435,8 @@ def gemv_workload(b: Bench, wtype, M, K, N, make_w, min_bytes=1.2e9, reps_floor=
     alg = wbytes + xq.numel() + 4 * N * M
     out = {"us_per_launch": sec / launches * 1e6, "bytes_per_launch": alg,
            "gbs": alg * launches / sec / 1e9, "frac_hbm": alg * launches / sec / 1e9 / HBM_PEAK_GBS,
-           "tops": 2 * M * N * K * launches / sec / 1e12, "copies": copies}
+           "tops": 2 * M * N * K * launches / sec / 1e12, "copies": copies,
+           "kernel_family": kernel_family(Q, wtype, M, N, K)}
     if read_floor and wbytes % 16 == 0:
         # the same weight bytes, same rotation, read by qmm_probe_read alone
         sink = torch.zeros(PROBE_SINK_WORDS, dtype=torch.int32, device=b.dev)

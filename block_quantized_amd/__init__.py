@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
             "qmm_mul_mat": (I, [I, P, P, P, I64, I64, I64, P]),
             "qmm_mul_mat_algo": (I, [I, P, P, P, I64, I64, I64, I, P]),
             "qmm_mul_mat_multi": (I, [I, I, P, P, P, P, I, I64, I64, P]),
+            "qmm_mul_mat_choice": (I, [I, I64, I64, I64]),
             "qmm_strerror": (ctypes.c_char_p, [I]),
             "qmm_probe_read": (I, [P, I64, P, I, P]),
             "qmm_probe_mfma": (I, [I, I64, P, P]),
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("qmm_block_size", "qmm_block_bytes", "qmm_row_bytes", "qmm_vec_dot_type", "qmm_quantize_act",
             "qmm_quantize", "qmm_dequantize", "qmm_mul_mat", "qmm_mul_mat_algo", "qmm_mul_mat_multi",
+            "qmm_mul_mat_choice",
             "qmm_strerror", "qmm_probe_read", "qmm_probe_mfma", "qmm_probe_mfma_ops",
             "qmm_probe_mfma16", "qmm_probe_mfma16_ops")
 
@@ -128,6 +130,10 @@ def qmm_mul_mat(wtype, W, xq, y, M, N, K, stream=None) -> int:
 
 def qmm_mul_mat_algo(wtype, W, xq, y, M, N, K, algo, stream=None) -> int:
     return lib().qmm_mul_mat_algo(wtype, _ptr(W), _ptr(xq), _ptr(y), M, N, K, algo, _stream(stream))
+
+
+def qmm_mul_mat_choice(wtype, M, N, K) -> int:
+    return lib().qmm_mul_mat_choice(wtype, M, N, K)
 
 
 def qmm_mul_mat_multi(wtype, count, W, y, M, x, x_is_f32, N, K, stream=None) -> int:

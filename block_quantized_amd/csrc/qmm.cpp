@@ -122,6 +122,13 @@ int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y, int64_t
     return hip_status(gemm ? launch_gemm(wtype, W, xq, y, M, N, K, s) : launch_gemv(wtype, W, xq, y, M, N, K, s));
 }
 
+int qmm_mul_mat_choice(int wtype, int64_t M, int64_t N, int64_t K) {
+    if (!is_type(wtype) || !is_weight(wtype)) return 0;
+    const int xt = qmm_vec_dot_type(wtype);
+    if (check_dims(wtype, M, K) || check_dims(xt, N, K) || M > INT_MAX || N > INT_MAX || K > kMaxK) return 0;
+    return gemm_supported(wtype) && N > gemm_min_rows(wtype, M) ? 2 : 1;
+}
+
 int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
                 void* stream) {
     return qmm_mul_mat_algo(wtype, W, xq, y, M, N, K, 0, stream);

@@ -159,6 +159,12 @@ int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y,
 int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y,
                      int64_t M, int64_t N, int64_t K, int algo, void* stream);
 
+/* The kernel family the automatic choice of qmm_mul_mat takes for these
+ * sizes: 1 = GEMV kernels, 2 = int8-MFMA GEMM kernels (for Q4_K with
+ * N <= 32 the narrow ones); 0 for a type or shape qmm_mul_mat would reject.
+ * Host logic only: no GPU work, no pointers. */
+int qmm_mul_mat_choice(int wtype, int64_t M, int64_t N, int64_t K);
+
 /* Several weight matrices that share K and the activation rows, in one
  * launch: e.g. the q, k and v projections of a layer, or its gate and up
  * projections, which all read the same normalized activations.  Each

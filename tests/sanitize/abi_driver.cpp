@@ -157,6 +157,12 @@ int main() {
     EXPECT(qmm_probe_mfma16(512, 0, sink, nullptr), QMM_ERR_SHAPE, 0);
     if (qmm_probe_mfma16_ops(2, 3) != 2LL * 32 * 3 * 32768 || qmm_probe_mfma16_ops(65537, 1) != 0) ++failures;
 
+    // ---- the automatic kernel choice (host logic)
+    if (qmm_mul_mat_choice(QMM_Q4_K, 14336, 2, 4096) != 1 || qmm_mul_mat_choice(QMM_Q4_K, 14336, 3, 4096) != 2 ||
+        qmm_mul_mat_choice(QMM_Q8_K, 64, 1, 256) != 0 || qmm_mul_mat_choice(QMM_Q4_0, 64, 1, 48) != 0 ||
+        qmm_mul_mat_choice(QMM_Q4_0, int64_t(1) << 40, 1, 32) != 0)
+        ++failures;
+
     // ---- status text
     for (int c = -8; c <= 1; ++c)
         if (!qmm_strerror(c) || !qmm_strerror(c)[0]) ++failures;

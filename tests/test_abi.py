@@ -130,6 +130,30 @@ def test_multi_errors_cpu(L):
     assert mm(Q.QMM_Q4_0, 1, [A], [A], [4], A, 1, 1, 96, S) == Q.QMM_ERR_UNSUPPORTED
 
 
+def test_mul_mat_choice_cpu(L):
+    # the automatic GEMV / GEMM switch of qmm_mul_mat, at the crossovers
+    # measured on MI355X (host logic: no GPU needed)
+    ch = Q.qmm_mul_mat_choice
+    assert [ch(Q.QMM_Q4_K, 14336, n, 4096) for n in (1, 2, 3, 8)] == [1, 1, 2, 2]
+    assert [ch(Q.QMM_Q4_K, 4096, n, 4096) for n in (1, 2, 32)] == [1, 2, 2]
+    assert [ch(Q.QMM_Q4_K, 1000, n, 4096) for n in (7, 8)] == [1, 2]
+    assert [ch(Q.QMM_Q6_K, 128256, n, 4096) for n in (8, 9, 32)] == [1, 2, 2]
+    assert [ch(Q.QMM_Q6_K, 4096, n, 14336) for n in (20, 21)] == [1, 2]
+    assert [ch(Q.QMM_Q4_0, 4096, n, 4096) for n in (36, 37)] == [1, 2]
+    assert [ch(Q.QMM_Q4_0, 14336, n, 4096) for n in (18, 19)] == [1, 2]
+    assert [ch(Q.QMM_Q8_0, 4096, n, 4096) for n in (32, 33)] == [1, 2]
+    assert [ch(Q.QMM_Q8_0, 14336, n, 4096) for n in (12, 13)] == [1, 2]
+    assert [ch(Q.QMM_Q5_0, 4096, n, 4096) for n in (36, 37)] == [1, 2]
+    assert [ch(Q.QMM_Q5_0, 14336, n, 4096) for n in (15, 16)] == [1, 2]
+    # what qmm_mul_mat rejects
+    assert ch(Q.QMM_Q8_K, 4096, 1, 4096) == 0           # not a weight type
+    assert ch(0, 4096, 1, 4096) == 0
+    assert ch(Q.QMM_Q4_K, 4096, 1, 4000) == 0           # K % 256
+    assert ch(Q.QMM_Q4_0, 0, 1, 4096) == 0
+    assert ch(Q.QMM_Q4_0, 64, 0, 4096) == 0
+    assert ch(Q.QMM_Q4_0, 64, 1, 65536 + 32) == 0       # K beyond the supported range
+
+
 def test_probe_errors_cpu(L):
     assert Q.qmm_probe_read(0, 64, A, 0, S) == Q.QMM_ERR_NULL
     assert Q.qmm_probe_read(A, 64, 0, 0, S) == Q.QMM_ERR_NULL
