@@ -176,3 +176,21 @@ def test_error_leaves_output_untouched():
     y = torch.full((4,), 7.0, device="cuda")
     assert Q.qmm_mul_mat(Q.QMM_Q4_0, W, xq, y, 4, 1, 48) == Q.QMM_ERR_SHAPE
     assert torch.all(y == 7.0).item()
+
+
+@pytest.mark.parametrize("wt", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0, Q.QMM_Q4_K, Q.QMM_Q6_K])
+@pytest.mark.parametrize("M", [1000, 4096, 8200])
+def test_automatic_choice_at_its_switch(wt, M):
+    # qmm_mul_mat on both sides of the GEMV / GEMM switch it reports; all
+    # outputs written, sampled rows (one per 32-row tile) compared
+    g = np.random.default_rng(100 + wt + M)
+    K = 512
+    W = make_weights(g, wt, M, K)
+    ch = [Q.qmm_mul_mat_choice(wt, M, n, K) for n in range(1, 41)]
+    assert ch[0] == 1 and set(ch) == {1, 2}
+    t = ch.index(2)  # the first N (minus one) that takes the GEMM
+    assert all(c == 1 for c in ch[:t]) and all(c == 2 for c in ch[t:])
+    for N in (t, t + 1):
+        x = g.standard_normal((N, K), dtype=np.float32)
+        say("auto switch", wt, M, N, "gemv" if ch[N - 1] == 1 else "gemm")
+        check(wt, W, x, M, N, K, rows=tile_rows(M), algo=0, what=f"type {wt} M={M} N={N}")
