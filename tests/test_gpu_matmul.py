@@ -194,3 +194,22 @@ def test_automatic_choice_at_its_switch(wt, M):
         x = g.standard_normal((N, K), dtype=np.float32)
         say("auto switch", wt, M, N, "gemv" if ch[N - 1] == 1 else "gemm")
         check(wt, W, x, M, N, K, rows=tile_rows(M), algo=0, what=f"type {wt} M={M} N={N}")
+
+
+@pytest.mark.parametrize("wt", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0, Q.QMM_Q4_K, Q.QMM_Q6_K])
+def test_seeded_random_shapes_every_kernel_family(wt):
+    # 12 seeded random shapes per type (ragged M and N, K any multiple of the
+    # block, up to 4096), each through the automatic choice and both kernel
+    # families; sampled rows (one per 32-row tile) against the oracle
+    g = np.random.default_rng(1000 + wt)
+    B = 256 if wt in (Q.QMM_Q4_K, Q.QMM_Q6_K) else 32
+    for case in range(12):
+        M = int(g.integers(1, 3000))
+        N = int(g.integers(1, 80))
+        K = B * int(g.integers(1, 4096 // B + 1))
+        W = make_weights(g, wt, M, K)
+        x = g.standard_normal((N, K), dtype=np.float32) * np.float32(10.0 ** g.uniform(-3, 3))
+        for algo in (0, 1, 2):
+            say("random shape", wt, case, M, N, K, "algo", algo)
+            check(wt, W, x, M, N, K, rows=tile_rows(M, seed=case), algo=algo,
+                  what=f"type {wt} case {case} {M}x{K} N={N} algo {algo}")
