@@ -110,7 +110,13 @@ struct RoundTag {
 template <int WT, int NC, bool XF, class Hook>
 __device__ __forceinline__ void stage_x(const uint8_t* xq, int G, uint8_t* xl, Hook&& after_loads) {
     constexpr bool kQ80 = (WT == QMM_Q4_0 || WT == QMM_Q5_0 || WT == QMM_Q8_0);
-    constexpr int KB = XF ? 1 : 4;  // items per thread per round
+    // One item per thread per round.  With four (the pre-quantized x once
+    // took 76 registers per thread for it) the compiler reused load
+    // destinations and waited for x loads inside the issue sequence: batch 1,
+    // Q4_K 14336x4096 9.8 -> 9.2 us, 4096x14336 10.0 -> 9.2 us, Q8_0 2048x2048
+    // 3.72 -> 3.64 us (measured on MI355X).  More rounds, when needed, run
+    // before the W prefetch (below).
+    constexpr int KB = 1;
     const int nitems = kQ80 ? NC * G * 8 : NC * G * 4;
     const int step = KB * blockDim.x;
     // A wave issues its loads when any of its lanes has an item (a lane past
