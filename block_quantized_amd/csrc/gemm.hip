@@ -44,6 +44,7 @@
 namespace qmm {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 // 4, 8 and 16 bytes at a 2-byte-aligned address (Q6_K super-blocks are 210
 // bytes, Q5_0 and Q8_0 blocks 22 and 34)
@@ -657,10 +658,13 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // 32-value blocks with one fp16 scale each, against Q8_0 activations.  The
 // weight codes enter the MFMA as int8 (q - 8, q - 16 or q itself), one
 // v_mfma_i32_32x32x32_i8 per block and activation tile, and each block's
-// integer tile is scaled by d_w * d_x in fp32 (the scales change every 32
-// values, so this epilogue, not the matrix core, bounds the kernel).
+// integer tile is scaled by d_w * d_x in fp32.  The scales change every 32
+// values, so this epilogue, not the matrix core, bounds the kernel: the tile
+// of products d_x[n] * d_w[m] comes from the matrix core too (one fp16 MFMA
+// on one-hot operands, exact), which leaves two VALU operations per output
+// and block (convert, fused multiply-add).
 // K runs in chunks of 4 blocks; the activation chunk of 64 rows is staged in
-// LDS (codes at row stride 144, scales as [block][row] floats).
+// LDS (codes at row stride 144, scales as [block][row] fp16 bits).
 template <int WT>
 struct Q32W;  // per-lane weight operand of one block: row c, values 16h .. 16h+15
 template <>
@@ -726,6 +730,21 @@ struct Q32W<QMM_Q5_0> {
     }
 };
 
+// One-hot fp16 operand of v_mfma_f32_32x32x8_f16: the fp16 in the low half of
+// `bits` at the lane's first K slot, zeros in the other three.  With the A
+// lane of row n holding d_x[n] and the B lane of column m holding d_w[m] (and
+// the lanes of the other K half all zero), the product tile is d_x[n] d_w[m],
+// exact in fp32 (two 11-bit significands).
+__device__ __forceinline__ v4h onehot_f16(uint32_t bits) {
+    return __builtin_bit_cast(v4h, ((v2i){(int)bits, 0}));
+}
+
+// K parts of the kernel on small grids: 4 (four waves per SIMD, within the
+// 128 VGPRs that allows), but 2 for Q8_0, whose next-chunk weight registers
+// (17 per lane) do not fit that budget.
+template <int WT>
+constexpr int kSplitQ32 = WT == QMM_Q8_0 ? 2 : 4;
+
 // KS = 2 or 4 splits the chunks between KS groups of 4 waves, as in the Q4_K
 // kernel (the launcher takes it only when the chunks are full and their
 // count is a multiple of KS).  The partial sums are added through LDS in a
@@ -740,7 +759,9 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
     constexpr int CS = 32 * CB + 16;        // LDS row stride of a chunk's codes
     static_assert(KS == 1 || KS == 2 || KS == 4, "K is split in 1, 2 or 4 parts");
     __shared__ __attribute__((aligned(16))) uint8_t s_codes_all[KS][2][BN][CS];
-    __shared__ __attribute__((aligned(16))) float s_dx_all[KS][2][CB][BN];
+    // fp16 bits of the activation scales; entries BN .. 2 BN - 1 stay zero (the
+    // scale operand of the lanes in the second K half)
+    __shared__ __attribute__((aligned(16))) uint16_t s_dx_all[KS][2][CB][2 * BN];
 
     const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
     const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);  // K part
@@ -771,7 +792,7 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
         uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][32 * jb]);
         dst[0] = make_uint4(xq0.x, xq0.y, xq0.z, xq0.w);
         dst[1] = make_uint4(xq1.x, xq1.y, xq1.z, xq1.w);
-        s_dx[buf][jb][rn] = h2f(xdb);
+        s_dx[buf][jb][rn] = (uint16_t)xdb;
     };
     // Weights, WC (whole chunks, NB % CB == 0): the wave's 32 rows x CB blocks
     // as row-contiguous 8-byte pieces (consecutive lanes, consecutive pieces of
@@ -824,6 +845,12 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) yacc[t][r] = 0.f;
+    // the scale operands: d_x from LDS (lanes of the second K half read the
+    // zero entries), d_w masked to zero in those lanes
+    const int dxl = c + (h ? BN : 0);
+    const uint32_t hmask = h ? 0u : 0xFFFFu;
+#pragma unroll
+    for (int i = tid; i < 2 * CB * BN; i += 256) s_dx[i / (CB * BN)][(i / BN) % CB][BN + i % BN] = 0;
 
     // this K part's chunks
     const int nper = (nch + (tail ? 1 : 0)) / KS, ch0 = kh * nper;
@@ -841,55 +868,46 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
     __syncthreads();
     for (int i = 0; i < nper; ++i) {
         const int ch = ch0 + i, buf = i & 1;
-        Q32W<WT> w[CB];
+        Q32W<WT> wc_[WC ? 1 : CB];  // without WC: this chunk's blocks, loaded a chunk ahead
         if constexpr (WC) {
             w_put();  // this chunk's weights (the previous chunk's reads of the region are done)
-#pragma unroll
-            for (int j = 0; j < CB; ++j) w[j].load(swc + c * RBc + j * Q32W<WT>::kBytes, h);
         } else {
 #pragma unroll
-            for (int j = 0; j < CB; ++j) w[j] = wn[j];
+            for (int j = 0; j < CB; ++j) wc_[j] = wn[j];
         }
         if (kAlwaysNext || i + 1 < nper) {
             x_load(ch + 1);
             w_load(ch + 1);
         }
         const int nb = (ch < nch) ? CB : tail;  // blocks in this chunk
-        // activation codes and scales are read from LDS one block ahead of their
-        // use (4096x4096, N = 512: Q4_0 52.6 -> 47 us)
-        v4i ar[2][2];
-        float4 dxr[2][2][4];
-        auto rd = [&](const int j, v4i (&aa)[2], float4 (&d)[2][4]) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                aa[t] = *reinterpret_cast<const v4i*>(&s_codes[buf][32 * t + c][32 * j + 16 * h]);
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd)
-                    d[t][qd] = *reinterpret_cast<const float4*>(&s_dx[buf][j][32 * t + 8 * qd + 4 * h]);
-            }
-        };
-        rd(0, ar[0], dxr[0]);
+        // Per block: the weight block, both tiles' activation codes and scales
+        // from LDS, then each tile's two matrix instructions and its epilogue
+        // in turn (one tile's results live at a time, so that four waves per
+        // SIMD fit their registers; the other waves hide the latencies).
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
-            if (j + 1 < CB) rd(j + 1, ar[(j + 1) & 1], dxr[(j + 1) & 1]);
-            if (j < nb) {
-                const v4i bq = w[j].operand(h);
-                const float dw = h2f(w[j].d);
-                // both tiles' products are issued before either is scaled
-                v16i pp[2];
+            Q32W<WT> wj;
+            if constexpr (WC) wj.load(swc + c * RBc + j * Q32W<WT>::kBytes, h);
+            else wj = wc_[j];
+            v4i ar[2];
+            uint32_t dxb[2];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) pp[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[j & 1][t], bq, (v16i){}, 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < 2; ++t) {
+                ar[t] = *reinterpret_cast<const v4i*>(&s_codes[buf][32 * t + c][32 * j + 16 * h]);
+                dxb[t] = s_dx[buf][j][32 * t + dxl];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (j < nb) {
+                const v4i bq = wj.operand(h);
+                const v4h dwo = onehot_f16(wj.d & hmask);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const v16i p = pp[t];
+                    const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[t], bq, (v16i){}, 0, 0, 0);
+                    const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(onehot_f16(dxb[t]), dwo, (v16f){}, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const float4 dx = dxr[j & 1][t][qd];
-                        const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) yacc[t][4 * qd + e] += (dw * dxa[e]) * (float)p[4 * qd + e];
-                    }
+                    for (int r = 0; r < 16; ++r) yacc[t][r] = __builtin_fmaf(sc[r], (float)p[r], yacc[t][r]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
@@ -1243,7 +1261,6 @@ bool gemm_supported(int wtype) {
 
 // Grids up to this many Q4_K tiles (one per CU) split K in two
 constexpr int64_t kSplitKMaxTiles = 256;
-constexpr int kSplitQ32 = 2;  // K parts of the Q4_0 / Q5_0 / Q8_0 kernel on such grids
 
 // Q4_K kernel with TN tiles per wave, W waves per K part, KS K parts (SB %
 // KS == 0), WPE waves per SIMD.
@@ -1272,24 +1289,23 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         const int64_t nb = (N + 63) / 64;
         const int NB = (int)(K / 32);
         const dim3 g = grid(mblocks * nb);
-        // K split in KQ32 parts (4 KQ32 waves per workgroup) for small grids
-        // whose 4-block chunks are full and a multiple of KQ32 in number
-        const bool split = mblocks * nb <= kSplitKMaxTiles && NB % (4 * kSplitQ32) == 0;
-        auto go = [&](auto k1, auto ks) {
-            if (split)
-                return launch(ks, g, dim3(256 * kSplitQ32), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks,
-                              (int)nb);
-            return launch(k1, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB, (int)mblocks, (int)nb);
+        // K split in KS parts (4 KS waves per workgroup) for small grids whose
+        // 4-block chunks are full and a multiple of KS in number; whole chunks
+        // otherwise take the row-contiguous weight staging (WC)
+        auto run = [&](auto wtc) {
+            constexpr int WT = decltype(wtc)::value, KS = kSplitQ32<WT>;
+            if (mblocks * nb <= kSplitKMaxTiles && NB % (4 * KS) == 0)
+                return launch(gemm_q32_kernel<WT, KS, true>, g, dim3(256 * KS), 0, s, w, x, y, (int)M, (int)N, NB,
+                              (int)mblocks, (int)nb);
+            if (NB % 4 == 0)
+                return launch(gemm_q32_kernel<WT, 1, true>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB,
+                              (int)mblocks, (int)nb);
+            return launch(gemm_q32_kernel<WT, 1, false>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB,
+                          (int)mblocks, (int)nb);
         };
-        const bool wc = NB % 4 == 0;  // whole chunks: row-contiguous weight staging
-        if (wtype == QMM_Q4_0)
-            return wc ? go(gemm_q32_kernel<QMM_Q4_0, 1, true>, gemm_q32_kernel<QMM_Q4_0, kSplitQ32, true>)
-                      : go(gemm_q32_kernel<QMM_Q4_0, 1, false>, gemm_q32_kernel<QMM_Q4_0, kSplitQ32, false>);
-        if (wtype == QMM_Q5_0)
-            return wc ? go(gemm_q32_kernel<QMM_Q5_0, 1, true>, gemm_q32_kernel<QMM_Q5_0, kSplitQ32, true>)
-                      : go(gemm_q32_kernel<QMM_Q5_0, 1, false>, gemm_q32_kernel<QMM_Q5_0, kSplitQ32, false>);
-        return wc ? go(gemm_q32_kernel<QMM_Q8_0, 1, true>, gemm_q32_kernel<QMM_Q8_0, kSplitQ32, true>)
-                  : go(gemm_q32_kernel<QMM_Q8_0, 1, false>, gemm_q32_kernel<QMM_Q8_0, kSplitQ32, false>);
+        if (wtype == QMM_Q4_0) return run(std::integral_constant<int, QMM_Q4_0>{});
+        if (wtype == QMM_Q5_0) return run(std::integral_constant<int, QMM_Q5_0>{});
+        return run(std::integral_constant<int, QMM_Q8_0>{});
     }
     if (wtype == QMM_Q6_K) {
         // weights staged through LDS; up to N = 32 (W read once, bound by

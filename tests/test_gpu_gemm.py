@@ -259,6 +259,38 @@ def test_gemm_q32_extremes_and_determinism(wtype):
 
 
 @pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
+@pytest.mark.parametrize("M,N,K", [(96, 40, 1024), (200, 70, 384), (40, 33, 96)])
+def test_gemm_q32_scale_extremes(wtype, M, N, K):
+    # fp16 block scales at the ends of their range, on both sides: the
+    # smallest and largest subnormals, the smallest normal, the largest finite
+    # value and -0 for the weights; subnormal and large activation scales.  The
+    # GEMM forms d_x d_w on the matrix core from fp16 operands, so subnormal
+    # inputs must not be flushed.  Shapes: K split in four parts (Q8_0: two),
+    # whole chunks without the split, a partial chunk.
+    g = np.random.default_rng(70 + wtype + K)
+    W = _q32_weights(g, wtype, M, K)
+    S = {Q.QMM_Q4_0: 18, Q.QMM_Q5_0: 22, Q.QMM_Q8_0: 34}[wtype]
+    bl = W.reshape(M, K // 32, S)
+    for r0, bits in ((0, 0x0001), (8, 0x03FF), (16, 0x0400), (24, 0x7BFF), (32, 0x8000)):
+        bl[r0:r0 + 8, :, 0] = bits & 0xFF
+        bl[r0:r0 + 8, :, 1] = bits >> 8
+    xq = O.quantize(O.Q8_0, g.standard_normal((N, K), dtype=np.float32))
+    xb = xq.reshape(N, K // 32, 34)
+    for r0, bits in ((0, 0x0001), (4, 0x0155), (8, 0x7BFF)):
+        xb[r0:r0 + 4, :, 0] = bits & 0xFF
+        xb[r0:r0 + 4, :, 1] = bits >> 8
+    print("gemm q32 scale extremes", wtype, M, N, K, flush=True)
+    ow = {Q.QMM_Q4_0: O.Q4_0, Q.QMM_Q5_0: O.Q5_0, Q.QMM_Q8_0: O.Q8_0}[wtype]
+    y_ref, T = O.mul_mat(ow, W, xq, M, N, K)
+    for algo in (2, 1):
+        y = run_product(wtype, W, xq, M, N, K, algo=algo)
+        assert np.all(np.isfinite(y))
+        assert_within_tolerance(y, y_ref, T, what=f"q32 scale extremes algo {algo}")
+    # products of two subnormal scales are far below the others but not zero
+    assert np.all(y_ref[0:4, 0:8] != 0)
+
+
+@pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
 def test_gemm_q32_bench_size_sampled(wtype):
     # the 4096 x 4096, N = 512 product the benchmark times (automatic choice):
     # every output written, one row of every 32-row tile against the oracle
