@@ -37,11 +37,11 @@ int check_dims(int t, int64_t rows, int64_t K) {
 int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 
 // Largest N for which the automatic choice keeps the GEMV kernels: the
-// crossovers measured on MI355X (4096- and 14336-wide rows).  The GEMV
-// decodes the weights once per activation row; the MFMA kernels once per 32
-// or 64 rows, with a fixed cost per super-block or block that the Q4_0, Q5_0
-// and Q8_0 kernels' per-block scaling makes large.
-int64_t gemm_min_rows(int wtype, int64_t M) {
+// crossovers measured on MI355X.  The GEMV decodes the weights once per
+// activation row (in groups of 8 rows); the MFMA kernels once per 32 or 64
+// rows, with a fixed cost per super-block or block that the Q4_0, Q5_0 and
+// Q8_0 kernels' per-block scaling makes large.
+int64_t gemm_min_rows(int wtype, int64_t M, int64_t K) {
     switch (wtype) {
     // the Q6_K GEMM has one 128-row workgroup per row block: below M = 8192
     // too few to fill the chip (4096x14336: 114 us at any N <= 32, against
@@ -51,12 +51,18 @@ int64_t gemm_min_rows(int wtype, int64_t M) {
     // 16-row tiles (M <= 8192) and from N = 3 on 32-row tiles (4096- and
     // 14336-row shapes); small matrices keep the GEMV longer
     case QMM_Q4_K: return M > 256 * 32 ? 2 : M >= 2048 ? 1 : 7;
-    // the Q4_0 / Q5_0 / Q8_0 GEMM takes about the same time for any N up
-    // to 512 on these shapes (4096 or 14336 rows, K = 4096: 44-60 us), while
-    // the GEMV's grows with M N; the switches are the measured crossovers
-    case QMM_Q4_0: return M > 8192 ? 18 : 36;
-    case QMM_Q8_0: return M > 8192 ? 12 : 32;
-    default: return M > 8192 ? 15 : 36;  // Q5_0
+    // Q4_0 / Q5_0 / Q8_0: while the grid has at most 256 tiles (M <= 8192 and
+    // N <= 64, or larger M and N up to 256 * 128 * 64 / M), the GEMM's time is
+    // its chain of 4-block chunks per wave, proportional to K and nearly
+    // independent of M and N (4096x4096: 36-37 / 42 / 47 us, 2048x8192: 66 /
+    // 79 / 89 us); the GEMV's grows by a step per group of activation rows,
+    // a longer one for small matrices (which leave SIMDs idle) and for large
+    // ones.  Measured switches: M > 8192 (14336x4096); K <= 2048 (2048x2048,
+    // 8192x2048); K <= 4096 with M >= 4096 (4096x4096) and below (1024x4096);
+    // wider rows (2048x8192).
+    case QMM_Q4_0: return M > 8192 ? 13 : K <= 2048 ? 18 : K <= 4096 ? (M >= 4096 ? 32 : 24) : 50;
+    case QMM_Q5_0: return M > 8192 ? 14 : K <= 2048 ? 19 : K <= 4096 ? (M >= 4096 ? 33 : 27) : 55;
+    default: return M > 8192 ? 11 : K <= 2048 ? 18 : K <= 4096 ? (M >= 4096 ? 33 : 30) : 54;  // Q8_0
     }
 }
 
@@ -118,7 +124,7 @@ int qmm_mul_mat_algo(int wtype, const void* W, const void* xq, float* y, int64_t
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool has_gemm = gemm_supported(wtype);
     if (algo == 2 && !has_gemm) return QMM_ERR_UNSUPPORTED;
-    const bool gemm = algo == 2 || (algo == 0 && has_gemm && N > gemm_min_rows(wtype, M));
+    const bool gemm = algo == 2 || (algo == 0 && has_gemm && N > gemm_min_rows(wtype, M, K));
     return hip_status(gemm ? launch_gemm(wtype, W, xq, y, M, N, K, s) : launch_gemv(wtype, W, xq, y, M, N, K, s));
 }
 
@@ -126,7 +132,7 @@ int qmm_mul_mat_choice(int wtype, int64_t M, int64_t N, int64_t K) {
     if (!is_type(wtype) || !is_weight(wtype)) return 0;
     const int xt = qmm_vec_dot_type(wtype);
     if (check_dims(wtype, M, K) || check_dims(xt, N, K) || M > INT_MAX || N > INT_MAX || K > kMaxK) return 0;
-    return gemm_supported(wtype) && N > gemm_min_rows(wtype, M) ? 2 : 1;
+    return gemm_supported(wtype) && N > gemm_min_rows(wtype, M, K) ? 2 : 1;
 }
 
 int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y, int64_t M, int64_t N, int64_t K,

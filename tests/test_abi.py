@@ -139,12 +139,12 @@ def test_mul_mat_choice_cpu(L):
     assert [ch(Q.QMM_Q4_K, 1000, n, 4096) for n in (7, 8)] == [1, 2]
     assert [ch(Q.QMM_Q6_K, 128256, n, 4096) for n in (8, 9, 32)] == [1, 2, 2]
     assert [ch(Q.QMM_Q6_K, 4096, n, 14336) for n in (20, 21)] == [1, 2]
-    assert [ch(Q.QMM_Q4_0, 4096, n, 4096) for n in (36, 37)] == [1, 2]
-    assert [ch(Q.QMM_Q4_0, 14336, n, 4096) for n in (18, 19)] == [1, 2]
-    assert [ch(Q.QMM_Q8_0, 4096, n, 4096) for n in (32, 33)] == [1, 2]
-    assert [ch(Q.QMM_Q8_0, 14336, n, 4096) for n in (12, 13)] == [1, 2]
-    assert [ch(Q.QMM_Q5_0, 4096, n, 4096) for n in (36, 37)] == [1, 2]
-    assert [ch(Q.QMM_Q5_0, 14336, n, 4096) for n in (15, 16)] == [1, 2]
+    # Q4_0 / Q5_0 / Q8_0: by rows above 8192, else by K and M
+    for wt, t in ((Q.QMM_Q4_0, (13, 18, 32, 24, 50)), (Q.QMM_Q5_0, (14, 19, 33, 27, 55)),
+                  (Q.QMM_Q8_0, (11, 18, 33, 30, 54))):
+        for (M, K), tm in zip(((14336, 4096), (8192, 2048), (4096, 4096), (1024, 4096), (2048, 8192)), t):
+            assert [ch(wt, M, n, K) for n in (tm, tm + 1)] == [1, 2], (wt, M, K)
+        assert ch(wt, 8193, 40, 32768) == 2 and ch(wt, 4096, 33, 512) == 2
     # what qmm_mul_mat rejects
     assert ch(Q.QMM_Q8_K, 4096, 1, 4096) == 0           # not a weight type
     assert ch(0, 4096, 1, 4096) == 0
