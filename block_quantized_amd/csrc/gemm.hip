@@ -739,11 +739,10 @@ __device__ __forceinline__ v4h onehot_f16(uint32_t bits) {
     return __builtin_bit_cast(v4h, ((v2i){(int)bits, 0}));
 }
 
-// K parts of the kernel on small grids: 4 (four waves per SIMD, within the
-// 128 VGPRs that allows), but 2 for Q8_0, whose next-chunk weight registers
-// (17 per lane) do not fit that budget.
-template <int WT>
-constexpr int kSplitQ32 = WT == QMM_Q8_0 ? 2 : 4;
+// K parts of the kernel on small grids: 4, four waves per SIMD (within the
+// 128 VGPRs that allows; Q8_0, with 17 registers of next-chunk weights per
+// lane, spills one).
+constexpr int kSplitQ32 = 4;
 
 // KS = 2 or 4 splits the chunks between KS groups of 4 waves, as in the Q4_K
 // kernel (the launcher takes it only when the chunks are full and their
@@ -777,16 +776,22 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
     const int nch = NB / CB, tail = NB % CB;  // full chunks; blocks in the last, partial one
 
     // activation staging: thread = (row rn, block jb) of the chunk
+    // through a buffer descriptor over the workgroup's activation rows that
+    // exist (rows past N read row N - 1): a 32-bit lane offset and no 64-bit
+    // addresses in registers
     const int rn = tid >> 2, jb = tid & 3;
-    const uint8_t* xrow = X + (int64_t)min(n0 + rn, N - 1) * NB * kQ8_0Bytes;
-    u32x4_a2 xq0, xq1;
+    const int xrowB = NB * kQ8_0Bytes;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(X) + (int64_t)n0 * xrowB, (short)0, min(BN, N - n0) * xrowB, kBufferWord3);
+    const unsigned xvo = (unsigned)(min(rn, N - 1 - n0) * xrowB);
+    u32x4 xq0, xq1;
     uint32_t xdb;
     auto x_load = [&](int ch) {
         const int blk = min(ch * CB + jb, NB - 1);  // a partial chunk repeats its last block
-        const uint8_t* p = xrow + (int64_t)blk * kQ8_0Bytes;
-        xdb = *reinterpret_cast<const uint16_t*>(p);
-        xq0 = *reinterpret_cast<const u32x4_a2*>(p + 2);
-        xq1 = *reinterpret_cast<const u32x4_a2*>(p + 18);
+        const unsigned o = xvo + (unsigned)(blk * kQ8_0Bytes);
+        xdb = __builtin_amdgcn_raw_buffer_load_b16(xrs, o, 0, 0);
+        xq0 = __builtin_amdgcn_raw_buffer_load_b128(xrs, o + 2, 0, 0);
+        xq1 = __builtin_amdgcn_raw_buffer_load_b128(xrs, o + 18, 0, 0);
     };
     auto x_store = [&](int buf) {
         uint4* dst = reinterpret_cast<uint4*>(&s_codes[buf][rn][32 * jb]);
@@ -808,11 +813,13 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
     uint8_t* const swc = s_wc_all[kh][wave];
     const int64_t rowWB = (int64_t)NB * Q32W<WT>::kBytes;
     u32x2 wpc[WC ? PW : 1];
-    // the wave's first row that exists (uniform) and each piece's 32-bit
-    // offset from it (rows past M read row M - 1; with K <= 65536 the offsets
-    // stay below 2^22)
+    // the wave's first row that exists (uniform), a buffer descriptor over
+    // its rows that exist, and each piece's 32-bit offset from that row (rows
+    // past M read row M - 1; with K <= 65536 the offsets stay below 2^22)
     const int wr0 = __builtin_amdgcn_readfirstlane(min(m0, M - 1));
-    const uint8_t* const wwave = W + (int64_t)wr0 * rowWB;
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W) + (int64_t)wr0 * rowWB, (short)0,
+        __builtin_amdgcn_readfirstlane(min(32, M - wr0)) * (int)rowWB, kBufferWord3);
     uint32_t woff[WC ? PW : 1];
     if constexpr (WC) {
 #pragma unroll
@@ -824,9 +831,12 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
     Q32W<WT> wn[WC ? 1 : CB];
     auto w_load = [&](int ch) {
         if constexpr (WC) {
-            const uint8_t* wb = wwave + (int64_t)min(ch, NB / CB - 1) * RBc;
+            const int so = min(ch, NB / CB - 1) * RBc;  // the chunk, in the scalar offset
 #pragma unroll
-            for (int i = 0; i < PW; ++i) wpc[i] = *reinterpret_cast<const u32x2*>(wb + woff[i]);
+            for (int i = 0; i < PW; ++i) {
+                const v2i v = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(wrs, woff[i], so, 0));
+                wpc[i] = (u32x2){(uint32_t)v.x, (uint32_t)v.y};
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < CB; ++j) wn[j].load(wrow + (int64_t)min(ch * CB + j, NB - 1) * Q32W<WT>::kBytes, h);
@@ -1293,7 +1303,7 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         // 4-block chunks are full and a multiple of KS in number; whole chunks
         // otherwise take the row-contiguous weight staging (WC)
         auto run = [&](auto wtc) {
-            constexpr int WT = decltype(wtc)::value, KS = kSplitQ32<WT>;
+            constexpr int WT = decltype(wtc)::value, KS = kSplitQ32;
             if (mblocks * nb <= kSplitKMaxTiles && NB % (4 * KS) == 0)
                 return launch(gemm_q32_kernel<WT, KS, true>, g, dim3(256 * KS), 0, s, w, x, y, (int)M, (int)N, NB,
                               (int)mblocks, (int)nb);

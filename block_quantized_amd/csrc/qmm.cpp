@@ -54,15 +54,15 @@ int64_t gemm_min_rows(int wtype, int64_t M, int64_t K) {
     // Q4_0 / Q5_0 / Q8_0: while the grid has at most 256 tiles (M <= 8192 and
     // N <= 64, or larger M and N up to 256 * 128 * 64 / M), the GEMM's time is
     // its chain of 4-block chunks per wave, proportional to K and nearly
-    // independent of M and N (4096x4096: 36-37 / 42 / 47 us, 2048x8192: 66 /
-    // 79 / 89 us); the GEMV's grows by a step per group of activation rows,
+    // independent of M and N (4096x4096: 33-34 / 39-40 / 39 us, 2048x8192:
+    // 61-66 / 72-77 / 71-78 us); the GEMV's grows by a step per group of activation rows,
     // a longer one for small matrices (which leave SIMDs idle) and for large
     // ones.  Measured switches: M > 8192 (14336x4096); K <= 2048 (2048x2048,
     // 8192x2048); K <= 4096 with M >= 4096 (4096x4096) and below (1024x4096);
     // wider rows (2048x8192).
-    case QMM_Q4_0: return M > 8192 ? 13 : K <= 2048 ? 18 : K <= 4096 ? (M >= 4096 ? 32 : 24) : 50;
-    case QMM_Q5_0: return M > 8192 ? 14 : K <= 2048 ? 19 : K <= 4096 ? (M >= 4096 ? 33 : 27) : 55;
-    default: return M > 8192 ? 11 : K <= 2048 ? 18 : K <= 4096 ? (M >= 4096 ? 33 : 30) : 54;  // Q8_0
+    case QMM_Q4_0: return M > 8192 ? 12 : K <= 2048 ? 17 : K <= 4096 ? (M >= 4096 ? 28 : 23) : 47;
+    case QMM_Q5_0: return M > 8192 ? 12 : K <= 2048 ? 19 : K <= 4096 ? (M >= 4096 ? 32 : 26) : 51;
+    default: return M > 8192 ? 10 : K <= 2048 ? 17 : K <= 4096 ? 26 : 45;  // Q8_0
     }
 }
 

@@ -145,10 +145,10 @@ int qmm_dequantize(int type, const void* blocks, float* out, int64_t rows, int64
  * MI355X: for Q6_K N > 8 when M > 8192, else N > 20; for Q4_K N > 1 when
  * 2048 <= M <= 8192, N > 2 when M > 8192, else N > 7 (Q4_K with N <= 32
  * takes narrow MFMA kernels, on 32- or 16-row tiles, that split K over the
- * waves of a workgroup); for Q4_0 / Q5_0 / Q8_0, N > 13 / 14 / 11 when
- * M > 8192, else N > 18 / 19 / 18 when K <= 2048, N > 32 / 33 / 33 when
- * K <= 4096 and M >= 4096, N > 24 / 27 / 30 when K <= 4096 and M < 4096, and
- * N > 50 / 55 / 54 for wider rows. */
+ * waves of a workgroup); for Q4_0 / Q5_0 / Q8_0, N > 12 / 12 / 10 when
+ * M > 8192, else N > 17 / 19 / 17 when K <= 2048, N > 28 / 32 / 26 when
+ * K <= 4096 and M >= 4096, N > 23 / 26 / 26 when K <= 4096 and M < 4096, and
+ * N > 47 / 51 / 45 for wider rows. */
 int qmm_mul_mat(int wtype, const void* W, const void* xq, float* y,
                 int64_t M, int64_t N, int64_t K, void* stream);
 

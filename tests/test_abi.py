@@ -140,8 +140,8 @@ def test_mul_mat_choice_cpu(L):
     assert [ch(Q.QMM_Q6_K, 128256, n, 4096) for n in (8, 9, 32)] == [1, 2, 2]
     assert [ch(Q.QMM_Q6_K, 4096, n, 14336) for n in (20, 21)] == [1, 2]
     # Q4_0 / Q5_0 / Q8_0: by rows above 8192, else by K and M
-    for wt, t in ((Q.QMM_Q4_0, (13, 18, 32, 24, 50)), (Q.QMM_Q5_0, (14, 19, 33, 27, 55)),
-                  (Q.QMM_Q8_0, (11, 18, 33, 30, 54))):
+    for wt, t in ((Q.QMM_Q4_0, (12, 17, 28, 23, 47)), (Q.QMM_Q5_0, (12, 19, 32, 26, 51)),
+                  (Q.QMM_Q8_0, (10, 17, 26, 26, 45))):
         for (M, K), tm in zip(((14336, 4096), (8192, 2048), (4096, 4096), (1024, 4096), (2048, 8192)), t):
             assert [ch(wt, M, n, K) for n in (tm, tm + 1)] == [1, 2], (wt, M, K)
         assert ch(wt, 8193, 40, 32768) == 2 and ch(wt, 4096, 33, 512) == 2

@@ -124,7 +124,7 @@ def test_small_and_ragged_shapes(wt):
 
 @pytest.mark.parametrize("wt", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
 def test_auto_choice_wide_matrix_mid_batch(wt):
-    # M > 8192 moves the GEMV/GEMM switch of these types down to N > 13 (Q5_0: 14, Q8_0: 11)
+    # M > 8192 moves the GEMV/GEMM switch of these types down to N > 12 (Q8_0: 10)
     g = np.random.default_rng(90 + wt)
     M, N, K = 8200, 25, 512
     W = make_weights(g, wt, M, K)
