@@ -745,8 +745,8 @@ __device__ __forceinline__ v4h onehot_f16(uint32_t bits) {
 constexpr int kSplitQ32 = 4;
 
 // KS = 2 or 4 splits the chunks between KS groups of 4 waves, as in the Q4_K
-// kernel (the launcher takes it only when the chunks are full and their
-// count is a multiple of KS).  The partial sums are added through LDS in a
+// kernel (the launcher takes KS = kSplitQ32 only when the chunks are full and
+// their count is a multiple of KS).  The partial sums are added through LDS in a
 // fixed tree, (p0 + p2) + (p1 + p3) for four parts, so results are
 // deterministic.
 template <int WT, int KS, bool WC>
@@ -775,10 +775,10 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(con
     const uint8_t* wrow = W + (int64_t)mrow * NB * Q32W<WT>::kBytes;
     const int nch = NB / CB, tail = NB % CB;  // full chunks; blocks in the last, partial one
 
-    // activation staging: thread = (row rn, block jb) of the chunk
+    // activation staging: thread = (row rn, block jb) of the chunk, read
     // through a buffer descriptor over the workgroup's activation rows that
-    // exist (rows past N read row N - 1): a 32-bit lane offset and no 64-bit
-    // addresses in registers
+    // exist (rows past N read row N - 1), so the lane offset is 32-bit and no
+    // 64-bit addresses are held in registers
     const int rn = tid >> 2, jb = tid & 3;
     const int xrowB = NB * kQ8_0Bytes;
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
