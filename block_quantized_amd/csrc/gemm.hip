@@ -780,7 +780,7 @@ constexpr int kSplitQ32 = 4;
 // fixed tree, (p0 + p2) + (p1 + p3) for four parts, so results are
 // deterministic.
 template <int WT, int KS, bool WC>
-__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void gemm_q32_kernel(const uint8_t* __restrict__ W,
+__global__ __launch_bounds__(256 * KS, KS == 4 ? 1 : 2) void gemm_q32_kernel(const uint8_t* __restrict__ W,
                                                                  const uint8_t* __restrict__ X,
                                                                  float* __restrict__ Y, int M, int N, int NB,
                                                                  int mblk, int nblk) {
@@ -1330,12 +1330,17 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         const int NB = (int)(K / 32);
         const dim3 g = grid(mblocks * nb);
         // K split in KS parts (4 KS waves per workgroup) for small grids whose
-        // 4-block chunks are full and a multiple of KS in number; whole chunks
-        // otherwise take the row-contiguous weight staging (WC)
+        // 4-block chunks are full and a multiple of KS in number, so that a
+        // SIMD holds four waves: KS = 4 up to 256 tiles, 2 up to 512
+        // (8192x4096, N = 512: Q4_0 68.3 -> 63.9 us); whole chunks otherwise
+        // take the row-contiguous weight staging (WC)
         auto run = [&](auto wtc) {
             constexpr int WT = decltype(wtc)::value, KS = kSplitQ32;
             if (mblocks * nb <= kSplitKMaxTiles && NB % (4 * KS) == 0)
                 return launch(gemm_q32_kernel<WT, KS, true>, g, dim3(256 * KS), 0, s, w, x, y, (int)M, (int)N, NB,
+                              (int)mblocks, (int)nb);
+            if (mblocks * nb <= 2 * kSplitKMaxTiles && NB % 8 == 0)
+                return launch(gemm_q32_kernel<WT, 2, true>, g, dim3(512), 0, s, w, x, y, (int)M, (int)N, NB,
                               (int)mblocks, (int)nb);
             if (NB % 4 == 0)
                 return launch(gemm_q32_kernel<WT, 1, true>, g, dim3(256), 0, s, w, x, y, (int)M, (int)N, NB,

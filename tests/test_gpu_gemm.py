@@ -127,7 +127,10 @@ def run_q6k(W, xq, M, N, K, algo=2):
 @pytest.mark.parametrize("M,N,K", [(32, 32, 256), (1, 9, 256), (31, 33, 512), (130, 100, 768), (300, 32, 2048),
                                    (129, 65, 256), (77, 1, 256), (4100, 32, 4096), (64, 8, 1280),
                                    # N <= 32 with 11 / 9 / 4 super-blocks per row and ragged M
-                                   (33, 5, 2816), (9000, 17, 2304), (8200, 31, 1024)])
+                                   (33, 5, 2816), (9000, 17, 2304), (8200, 31, 1024),
+                                   # N > 32: K in two parts (ragged M and N), and a grid of more
+                                   # than 256 tiles that keeps K whole
+                                   (200, 70, 2048), (33000, 40, 512)])
 def test_gemm_q6k_shapes(M, N, K):
     g = np.random.default_rng(M * 5 + N * 17 + K)
     W = synth.q6_k_random(g, M, K)
@@ -216,7 +219,9 @@ def _q32_weights(g, wtype, M, K):
 
 @pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
 @pytest.mark.parametrize("M,N,K", [(32, 64, 128), (1, 9, 32), (31, 65, 96), (130, 100, 896), (300, 129, 1024),
-                                   (128, 512, 2048), (77, 1, 160), (16384, 65, 512), (16400, 65, 512)])
+                                   (128, 512, 2048), (77, 1, 160), (16384, 65, 512), (16400, 65, 512),
+                                   # 258 and 512 tiles: K in two parts
+                                   (16400, 100, 512), (8192, 512, 256)])
 def test_gemm_q32_shapes(wtype, M, N, K):
     g = np.random.default_rng(M * 11 + N * 3 + K + wtype)
     W = _q32_weights(g, wtype, M, K)
