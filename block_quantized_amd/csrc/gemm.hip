@@ -1361,9 +1361,10 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
                           (int)mblocks, 1);
         } else {
             const int64_t nb = (N + 63) / 64;
-            // grids of at most 256 tiles: K in two parts, two waves per SIMD
-            // (4096x14336, N = 512: 146 against 167 us)
-            if (mblocks * nb <= kSplitKMaxTiles && SB % 2 == 0)
+            // K in two parts: two waves per SIMD instead of one (N = 512:
+            // 4096x14336 146 against 167 us, 8192x14336 291 against 340 us;
+            // 128256x4096 at N = 64: 206 against 225 us)
+            if (SB % 2 == 0)
                 return launch(gemm_q6k_lds_kernel<2, 4, 2, 2>, grid(mblocks * nb), dim3(512), 0, s, w, x, y, (int)M,
                               (int)N, SB, (int)mblocks, (int)nb);
             return launch(gemm_q6k_lds_kernel<2, 4, 1>, grid(mblocks * nb), dim3(256), 0, s, w, x, y, (int)M, (int)N,

@@ -128,9 +128,9 @@ def run_q6k(W, xq, M, N, K, algo=2):
                                    (129, 65, 256), (77, 1, 256), (4100, 32, 4096), (64, 8, 1280),
                                    # N <= 32 with 11 / 9 / 4 super-blocks per row and ragged M
                                    (33, 5, 2816), (9000, 17, 2304), (8200, 31, 1024),
-                                   # N > 32: K in two parts (ragged M and N), and a grid of more
-                                   # than 256 tiles that keeps K whole
-                                   (200, 70, 2048), (33000, 40, 512)])
+                                   # N > 32: K in two parts (ragged M and N, and a grid of more
+                                   # than 256 tiles), and an odd super-block count that keeps K whole
+                                   (200, 70, 2048), (33000, 40, 512), (1000, 40, 768)])
 def test_gemm_q6k_shapes(M, N, K):
     g = np.random.default_rng(M * 5 + N * 17 + K)
     W = synth.q6_k_random(g, M, K)
