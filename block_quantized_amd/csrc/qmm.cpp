@@ -47,10 +47,11 @@ int64_t gemm_min_rows(int wtype, int64_t M, int64_t K) {
     // too few to fill the chip (4096x14336: 114 us at any N <= 32, against
     // 59-88 us for the GEMV at N = 9-16)
     case QMM_Q6_K: return M > 256 * 32 ? 8 : 20;
-    // the narrow MFMA kernels (weights staged through LDS) win from N = 2 on
-    // 16-row tiles (M <= 8192) and from N = 3 on 32-row tiles (4096- and
-    // 14336-row shapes); small matrices keep the GEMV longer
-    case QMM_Q4_K: return M > 256 * 32 ? 2 : M >= 2048 ? 1 : 7;
+    // the narrow MFMA kernels (weights staged through LDS) win from N = 3
+    // (measured at 1024, 2048, 4096 and 14336 rows with K = 4096 and at
+    // 4096x14336; at N = 2 the two tie or the GEMV wins); matrices of fewer
+    // than 1024 rows keep the GEMV up to N = 7
+    case QMM_Q4_K: return M >= 1024 ? 2 : 7;
     // Q4_0 / Q5_0 / Q8_0: while the grid has at most 256 tiles (M <= 8192 and
     // N <= 64, or larger M and N up to 256 * 128 * 64 / M), the GEMM's time is
     // its chain of 4-block chunks per wave, proportional to K and nearly

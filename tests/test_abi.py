@@ -135,7 +135,8 @@ def test_mul_mat_choice_cpu(L):
     # measured on MI355X (host logic: no GPU needed)
     ch = Q.qmm_mul_mat_choice
     assert [ch(Q.QMM_Q4_K, 14336, n, 4096) for n in (1, 2, 3, 8)] == [1, 1, 2, 2]
-    assert [ch(Q.QMM_Q4_K, 4096, n, 4096) for n in (1, 2, 32)] == [1, 2, 2]
+    assert [ch(Q.QMM_Q4_K, 4096, n, 4096) for n in (1, 2, 3, 32)] == [1, 1, 2, 2]
+    assert [ch(Q.QMM_Q4_K, 1024, n, 4096) for n in (2, 3)] == [1, 2]
     assert [ch(Q.QMM_Q4_K, 1000, n, 4096) for n in (7, 8)] == [1, 2]
     assert [ch(Q.QMM_Q6_K, 128256, n, 4096) for n in (8, 9, 32)] == [1, 2, 2]
     assert [ch(Q.QMM_Q6_K, 4096, n, 14336) for n in (20, 21)] == [1, 2]
