@@ -953,7 +953,11 @@ hipError_t gemv_typed(int nseg, const void* const* Ws, float* const* ys, const i
     const int64_t per_cu = (work + di.cus - 1) / di.cus;
     const int wpg = xf32 ? (per_cu >= 4 ? 4 : 2) : per_cu >= 8 ? 8 : per_cu >= 4 ? 4 : per_cu >= 2 ? 2 : 1;
     for (int64_t n0 = 0; n0 < N;) {
-        int nc = (int)(N - n0 < 8 ? N - n0 : 8);
+        // Q6_K in groups of at most 6 rows: its 7- and 8-row instances spill
+        // (4096x14336 at N = 12 / 16 / 24: 48 / 67 / 94 us against 65 / 87 /
+        // 128 us in groups of 8); the other types are fastest in groups of 8
+        constexpr int kMaxNC = WT == QMM_Q6_K ? 6 : 8;
+        int nc = (int)(N - n0 < kMaxNC ? N - n0 : kMaxNC);
         while (nc > 1 && (size_t)nc * a.G * XREC > di.lds) --nc;
         const size_t lds = (size_t)nc * a.G * XREC;
         if (lds > di.lds) return hipErrorInvalidValue;

@@ -44,11 +44,11 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 int64_t gemm_min_rows(int wtype, int64_t M, int64_t K) {
     switch (wtype) {
     // the Q6_K GEMM has one 128-row workgroup per row block: below M = 8192
-    // too few to fill the chip (4096x14336: 114-118 us at any N <= 32,
-    // against 46-109 us for the GEMV at N = 8-20).  Above, it takes the same
-    // time from N = 4 on (the 128256x4096 head: 113-117 us), while the GEMV's
-    // grows (115 us at N = 4, 280 us at N = 8)
-    case QMM_Q6_K: return M > 256 * 32 ? 4 : 20;
+    // too few to fill the chip (4096x14336: 118 us at any N <= 32, against
+    // 88 / 114 / 118 / 132 us for the GEMV in groups of 6 at N = 20 / 28 /
+    // 30 / 32).  Above, it takes the same time from N = 4 on (the 128256x4096
+    // head: 113-117 us), while the GEMV's grows (115 us at N = 4)
+    case QMM_Q6_K: return M > 256 * 32 ? 4 : 30;
     // the narrow MFMA kernels (weights staged through LDS) win from N = 3
     // (measured at 1024, 2048, 4096 and 14336 rows with K = 4096 and at
     // 4096x14336; at N = 2 the two tie or the GEMV wins); matrices of fewer
