@@ -775,10 +775,9 @@ __device__ __forceinline__ v4h onehot_f16(uint32_t bits) {
 constexpr int kSplitQ32 = 4;
 
 // KS = 2 or 4 splits the chunks between KS groups of 4 waves, as in the Q4_K
-// kernel (the launcher takes KS = kSplitQ32 only when the chunks are full and
-// their count is a multiple of KS).  The partial sums are added through LDS in a
-// fixed tree, (p0 + p2) + (p1 + p3) for four parts, so results are
-// deterministic.
+// kernel (the launcher takes KS > 1 only when the chunks are full and there
+// are at least KS of them).  The partial sums are added through LDS in a fixed
+// tree, (p0 + p2) + (p1 + p3) for four parts, so results are deterministic.
 template <int WT, int KS, bool WC>
 __global__ __launch_bounds__(256 * KS, KS == 4 ? 1 : 2) void gemm_q32_kernel(const uint8_t* __restrict__ W,
                                                                  const uint8_t* __restrict__ X,
@@ -892,8 +891,13 @@ __global__ __launch_bounds__(256 * KS, KS == 4 ? 1 : 2) void gemm_q32_kernel(con
 #pragma unroll
     for (int i = tid; i < 2 * CB * BN; i += 256) s_dx[i / (CB * BN)][(i / BN) % CB][BN + i % BN] = 0;
 
-    // this K part's chunks
-    const int nper = (nch + (tail ? 1 : 0)) / KS, ch0 = kh * nper;
+    // this K part's chunks: part kh takes chunks [kh TC / KS, (kh + 1) TC / KS)
+    // of the TC, so the parts differ by at most one chunk.  Every part runs
+    // the longest part's count of iterations, so that the workgroup's barriers
+    // pair up, and computes nothing in those past its own chunks (their loads
+    // are clamped to chunks that exist).
+    const int TC = nch + (tail ? 1 : 0);
+    const int ch0 = kh * TC / KS, nper = (kh + 1) * TC / KS - ch0, nit = (TC + KS - 1) / KS;
     // Q5_0 issues the next chunk's loads and LDS store unconditionally
     // (after the last chunk they re-read blocks that exist and fill a buffer
     // nobody reads).  With a branch around them the compiler's load waits must
@@ -906,7 +910,7 @@ __global__ __launch_bounds__(256 * KS, KS == 4 ? 1 : 2) void gemm_q32_kernel(con
     w_load(ch0);
     x_store(0);
     __syncthreads();
-    for (int i = 0; i < nper; ++i) {
+    for (int i = 0; i < nit; ++i) {
         const int ch = ch0 + i, buf = i & 1;
         Q32W<WT> wc_[WC ? 1 : CB];  // without WC: this chunk's blocks, loaded a chunk ahead
         if constexpr (WC) {
@@ -915,11 +919,11 @@ __global__ __launch_bounds__(256 * KS, KS == 4 ? 1 : 2) void gemm_q32_kernel(con
 #pragma unroll
             for (int j = 0; j < CB; ++j) wc_[j] = wn[j];
         }
-        if (kAlwaysNext || i + 1 < nper) {
+        if (kAlwaysNext || i + 1 < nit) {
             x_load(ch + 1);
             w_load(ch + 1);
         }
-        const int nb = (ch < nch) ? CB : tail;  // blocks in this chunk
+        const int nb = i >= nper ? 0 : (ch < nch) ? CB : tail;  // blocks in this chunk
         // Per block: the weight block, both tiles' activation codes and scales
         // from LDS, then each tile's two matrix instructions and its epilogue
         // in turn (one tile's results live at a time, so that four waves per
@@ -951,7 +955,7 @@ __global__ __launch_bounds__(256 * KS, KS == 4 ? 1 : 2) void gemm_q32_kernel(con
                 }
             }
         }
-        if (kAlwaysNext || i + 1 < nper) x_store(buf ^ 1);
+        if (kAlwaysNext || i + 1 < nit) x_store(buf ^ 1);
         __syncthreads();
     }
 
@@ -1330,16 +1334,16 @@ hipError_t launch_gemm(int wtype, const void* W, const void* xq, float* y, int64
         const int NB = (int)(K / 32);
         const dim3 g = grid(mblocks * nb);
         // K split in KS parts (4 KS waves per workgroup) for small grids whose
-        // 4-block chunks are full and a multiple of KS in number, so that a
-        // SIMD holds four waves: KS = 4 up to 256 tiles, 2 up to 512
-        // (8192x4096, N = 512: Q4_0 68.3 -> 63.9 us); whole chunks otherwise
-        // take the row-contiguous weight staging (WC)
+        // 4-block chunks are full and at least KS in number, so that a SIMD
+        // holds four waves: KS = 4 up to 256 tiles, 2 up to 512 (8192x4096,
+        // N = 512: Q4_0 68.3 -> 63.9 us); whole chunks otherwise take the
+        // row-contiguous weight staging (WC)
         auto run = [&](auto wtc) {
             constexpr int WT = decltype(wtc)::value, KS = kSplitQ32;
-            if (mblocks * nb <= kSplitKMaxTiles && NB % (4 * KS) == 0)
+            if (mblocks * nb <= kSplitKMaxTiles && NB % 4 == 0 && NB >= 4 * KS)
                 return launch(gemm_q32_kernel<WT, KS, true>, g, dim3(256 * KS), 0, s, w, x, y, (int)M, (int)N, NB,
                               (int)mblocks, (int)nb);
-            if (mblocks * nb <= 2 * kSplitKMaxTiles && NB % 8 == 0)
+            if (mblocks * nb <= 2 * kSplitKMaxTiles && NB % 4 == 0 && NB >= 8)
                 return launch(gemm_q32_kernel<WT, 2, true>, g, dim3(512), 0, s, w, x, y, (int)M, (int)N, NB,
                               (int)mblocks, (int)nb);
             if (NB % 4 == 0)

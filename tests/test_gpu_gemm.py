@@ -221,7 +221,11 @@ def _q32_weights(g, wtype, M, K):
 @pytest.mark.parametrize("M,N,K", [(32, 64, 128), (1, 9, 32), (31, 65, 96), (130, 100, 896), (300, 129, 1024),
                                    (128, 512, 2048), (77, 1, 160), (16384, 65, 512), (16400, 65, 512),
                                    # 258 and 512 tiles: K in two parts
-                                   (16400, 100, 512), (8192, 512, 256)])
+                                   (16400, 100, 512), (8192, 512, 256),
+                                   # chunks not a multiple of the parts: K in four
+                                   # parts of 1, 2, 2, 2 and 9, 10, 9, 10 chunks,
+                                   # in two parts of 1 and 2
+                                   (896, 24, 896), (4864, 100, 896), (300, 70, 4864), (500, 40, 384)])
 def test_gemm_q32_shapes(wtype, M, N, K):
     g = np.random.default_rng(M * 11 + N * 3 + K + wtype)
     W = _q32_weights(g, wtype, M, K)
@@ -264,14 +268,14 @@ def test_gemm_q32_extremes_and_determinism(wtype):
 
 
 @pytest.mark.parametrize("wtype", [Q.QMM_Q4_0, Q.QMM_Q5_0, Q.QMM_Q8_0])
-@pytest.mark.parametrize("M,N,K", [(96, 40, 1024), (200, 70, 384), (40, 33, 96)])
+@pytest.mark.parametrize("M,N,K", [(96, 40, 1024), (200, 70, 384), (70, 40, 128), (40, 33, 96)])
 def test_gemm_q32_scale_extremes(wtype, M, N, K):
     # fp16 block scales at the ends of their range, on both sides: the
     # smallest and largest subnormals, the smallest normal, the largest finite
     # value and -0 for the weights; subnormal and large activation scales.  The
     # GEMM forms d_x d_w on the matrix core from fp16 operands, so subnormal
-    # inputs must not be flushed.  Shapes: K split in four parts (Q8_0: two),
-    # whole chunks without the split, a partial chunk.
+    # inputs must not be flushed.  Shapes: K split in four parts, in two
+    # uneven parts, whole chunks without the split, a partial chunk.
     g = np.random.default_rng(70 + wtype + K)
     W = _q32_weights(g, wtype, M, K)
     S = {Q.QMM_Q4_0: 18, Q.QMM_Q5_0: 22, Q.QMM_Q8_0: 34}[wtype]
