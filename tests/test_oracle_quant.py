@@ -13,7 +13,7 @@ from zero, exact sums, zero block, sign and power-of-two symmetry).
 """
 import numpy as np
 import pytest
-from hypothesis import given, settings, strategies as st
+from hypothesis import example, given, settings, strategies as st
 from hypothesis.extra.numpy import arrays
 
 import oracle as O
@@ -76,12 +76,18 @@ def _check_rtn(x, d, q, B):
     # the element of largest magnitude lands on +-127
     i = np.abs(xb).argmax(axis=1)
     assert np.all(np.abs(qb[np.arange(len(i)), i][nz]) == 127)
-    # |x - d q| <= d/2, up to the rounding of d and of x*id (a few fp32 ulps).
-    # Where d is subnormal its own rounding (half the 2^-149 quantum, times
-    # up to 127 steps) adds to the bound.
+    # Blocks whose 1/d overflows fp32 (amax below about 127 / FLT_MAX): every
+    # x * id is +-Inf, so each nonzero value saturates to +-127 and zeros stay 0
+    # (0 * Inf is NaN, read as 0).
+    with np.errstate(divide="ignore", over="ignore"):
+        ovf = nz & ~np.isfinite(np.float32(1) / d.astype(np.float32))
+    assert np.array_equal(qb[ovf], (127 * np.sign(xb[ovf])).astype(np.int64))
+    # Elsewhere |x - d q| <= d/2, up to the rounding of d and of x*id (a few
+    # fp32 ulps).  Where d is subnormal its own rounding (half the 2^-149
+    # quantum, times up to 127 steps) adds to the bound.
     err = np.abs(xb - d[:, None] * qb)
     slack = np.where(d < 2.0 ** -126, 127 * 2.0 ** -150, 0.0)
-    assert np.all(err <= d[:, None] * (0.5 + 1e-5) + slack[:, None] + 1e-45)
+    assert np.all((err <= d[:, None] * (0.5 + 1e-5) + slack[:, None] + 1e-45)[~ovf])
     # zero blocks: d = 0 and q = 0
     assert np.all(qb[amax == 0] == 0) and np.all(d[amax == 0] == 0)
     assert np.all(np.abs(qb) <= 127)
@@ -149,6 +155,7 @@ def test_q8_k_hypothesis(x):
 
 @settings(max_examples=200, deadline=None)
 @given(arrays(np.float32, 32, elements=st.floats(-6e4, 6e4, width=32)))
+@example(np.array([2.0 ** -126] + [2.0 ** -149] * 31, np.float32))  # 1/d overflows
 def test_q8_0_hypothesis(x):
     b = O.quantize(O.Q8_0, x)
     amax = np.abs(x).max()
