@@ -50,10 +50,11 @@ int64_t gemm_min_rows(int wtype, int64_t M, int64_t K) {
     // head: 113-117 us), while the GEMV's grows (115 us at N = 4)
     case QMM_Q6_K: return M > 256 * 32 ? 4 : 30;
     // the narrow MFMA kernels (weights staged through LDS) win from N = 3
-    // (measured at 1024, 2048, 4096 and 14336 rows with K = 4096 and at
-    // 4096x14336; at N = 2 the two tie or the GEMV wins); matrices of fewer
-    // than 1024 rows keep the GEMV up to N = 7
-    case QMM_Q4_K: return M >= 1024 ? 2 : 7;
+    // (measured from 256 to 14336 rows with K = 4096, at 4096x14336, 1536x1536,
+    // 1536x8960 and 256x1536; at N = 2 the two tie or the GEMV wins).  Above
+    // 8192 rows with K < 4096 (8960x1536, 11008x2048, 16384x1536) the 32-row
+    // kernel has only a few super-blocks per wave and the GEMV wins up to N = 4
+    case QMM_Q4_K: return M > 8192 && K < 4096 ? 4 : 2;
     // Q4_0 / Q5_0 / Q8_0: while the grid has at most 256 tiles (M <= 8192 and
     // N <= 64, or larger M and N up to 256 * 128 * 64 / M), the GEMM's time is
     // its chain of 4-block chunks per wave, proportional to K and nearly

@@ -137,7 +137,10 @@ def test_mul_mat_choice_cpu(L):
     assert [ch(Q.QMM_Q4_K, 14336, n, 4096) for n in (1, 2, 3, 8)] == [1, 1, 2, 2]
     assert [ch(Q.QMM_Q4_K, 4096, n, 4096) for n in (1, 2, 3, 32)] == [1, 1, 2, 2]
     assert [ch(Q.QMM_Q4_K, 1024, n, 4096) for n in (2, 3)] == [1, 2]
-    assert [ch(Q.QMM_Q4_K, 1000, n, 4096) for n in (7, 8)] == [1, 2]
+    assert [ch(Q.QMM_Q4_K, 1000, n, 4096) for n in (2, 3)] == [1, 2]
+    assert [ch(Q.QMM_Q4_K, 256, n, 1536) for n in (2, 3)] == [1, 2]
+    assert [ch(Q.QMM_Q4_K, 8960, n, 1536) for n in (4, 5)] == [1, 2]
+    assert [ch(Q.QMM_Q4_K, 14336, n, 4096) for n in (2, 3)] == [1, 2]
     assert [ch(Q.QMM_Q6_K, 128256, n, 4096) for n in (4, 5, 32)] == [1, 2, 2]
     assert [ch(Q.QMM_Q6_K, 4096, n, 14336) for n in (30, 31)] == [1, 2]
     # Q4_0 / Q5_0 / Q8_0: by rows above 8192, else by K and M
