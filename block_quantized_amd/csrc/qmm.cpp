@@ -43,12 +43,15 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 // Q8_0 kernels' per-block scaling makes large.
 int64_t gemm_min_rows(int wtype, int64_t M, int64_t K) {
     switch (wtype) {
-    // the Q6_K GEMM has one 128-row workgroup per row block: below M = 8192
-    // too few to fill the chip (4096x14336: 118 us at any N <= 32, against
-    // 88 / 114 / 118 / 132 us for the GEMV in groups of 6 at N = 20 / 28 /
-    // 30 / 32).  Above, it takes the same time from N = 4 on (the 128256x4096
-    // head: 113-117 us), while the GEMV's grows (115 us at N = 4)
-    case QMM_Q6_K: return M > 256 * 32 ? 4 : 30;
+    // the Q6_K GEMM has one 128-row workgroup per row block, and its time is
+    // flat in N up to 32.  With about one row block per CU or more (32000x4096,
+    // the 128256x4096 and 151936x1536 heads) it wins from N = 5 at the latest;
+    // with 70-112 row blocks (8960x1536, 11008x2048, 14336x4096) once the GEMV
+    // needs a second group of 6 rows; below 8192 rows near N = 30 (4096x14336:
+    // 118 us at N <= 32 against 88 / 118 / 132 us at N = 20 / 30 / 32; 4096^2:
+    // about 25), and below 2048 rows (1536x8960: 12 workgroups, 72 us at
+    // N <= 32 and 104-106 us for N = 33-64) near N = 54
+    case QMM_Q6_K: return M > 24576 ? 4 : M > 8192 ? 6 : M < 2048 ? 54 : 30;
     // the narrow MFMA kernels (weights staged through LDS) win from N = 3
     // (measured from 256 to 14336 rows with K = 4096, at 4096x14336, 1536x1536,
     // 1536x8960 and 256x1536; at N = 2 the two tie or the GEMV wins).  Above

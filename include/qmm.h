@@ -142,7 +142,8 @@ int qmm_dequantize(int type, const void* blocks, float* out, int64_t rows, int64
  * block's 16-wide sums.  Accumulation is fp32.  Small N runs the
  * bandwidth-bound GEMV kernels (in groups of up to 8 activation rows), larger
  * N the int8-MFMA GEMM kernels; the switch is at the crossover measured on
- * MI355X: for Q6_K N > 4 when M > 8192, else N > 30; for Q4_K N > 4 when
+ * MI355X: for Q6_K N > 4 when M > 24576, N > 6 when 8192 < M <= 24576,
+ * N > 54 when M < 2048, else N > 30; for Q4_K N > 4 when
  * M > 8192 and K < 4096, else N > 2 (Q4_K with N <= 32
  * takes narrow MFMA kernels, on 32- or 16-row tiles, that split K over the
  * waves of a workgroup); for Q4_0 / Q5_0 / Q8_0, N > 12 / 12 / 10 when

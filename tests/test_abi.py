@@ -143,6 +143,10 @@ def test_mul_mat_choice_cpu(L):
     assert [ch(Q.QMM_Q4_K, 14336, n, 4096) for n in (2, 3)] == [1, 2]
     assert [ch(Q.QMM_Q6_K, 128256, n, 4096) for n in (4, 5, 32)] == [1, 2, 2]
     assert [ch(Q.QMM_Q6_K, 4096, n, 14336) for n in (30, 31)] == [1, 2]
+    assert [ch(Q.QMM_Q6_K, 32000, n, 4096) for n in (4, 5)] == [1, 2]
+    assert [ch(Q.QMM_Q6_K, 14336, n, 4096) for n in (6, 7)] == [1, 2]
+    assert [ch(Q.QMM_Q6_K, 8960, n, 1536) for n in (6, 7)] == [1, 2]
+    assert [ch(Q.QMM_Q6_K, 1536, n, 8960) for n in (54, 55)] == [1, 2]
     # Q4_0 / Q5_0 / Q8_0: by rows above 8192, else by K and M
     shapes = ((14336, 4096), (8960, 1536), (896, 896), (1536, 1536), (2048, 1024), (4864, 896),
               (8192, 2048), (4096, 4096), (1024, 4096), (896, 4864), (1536, 8960), (2048, 8192))

@@ -186,7 +186,7 @@ def test_automatic_choice_at_its_switch(wt, M):
     g = np.random.default_rng(100 + wt + M)
     K = 512
     W = make_weights(g, wt, M, K)
-    ch = [Q.qmm_mul_mat_choice(wt, M, n, K) for n in range(1, 41)]
+    ch = [Q.qmm_mul_mat_choice(wt, M, n, K) for n in range(1, 65)]
     assert ch[0] == 1 and set(ch) == {1, 2}
     t = ch.index(2)  # the first N (minus one) that takes the GEMM
     assert all(c == 1 for c in ch[:t]) and all(c == 2 for c in ch[t:])
