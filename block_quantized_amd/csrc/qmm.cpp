@@ -64,25 +64,30 @@ int64_t gemm_min_rows(int wtype, int64_t M, int64_t K) {
     // independent of M and N (4096x4096: 33-34 / 39-40 / 39 us, 2048x8192:
     // 61-66 / 72-77 / 71-78 us); the GEMV's grows by a step per group of activation rows,
     // a longer one for small matrices (which leave SIMDs idle) and for large
-    // ones.  Measured switches: M > 8192 (14336x4096, 8960x1536); K < 2048
+    // ones.  Measured switches: M > 24576 (32000x4096, 65536x2048: the GEMM
+    // has a row block per CU or more); M > 8192 (14336x4096, 8960x1536,
+    // 11008x2048); K < 2048
     // by rows (896x896; 1536x1536 and 2048x1024; 4864x896); K = 2048
     // (2048x2048, 8192x2048); K <= 4096 with M >= 4096 (4096x4096) and below
     // (1024x4096); wider rows, with M < 2048 (896x4864, 1536x8960) and above
     // (2048x8192).
     case QMM_Q4_0:
-        return M > 8192   ? 12
+        return M > 24576  ? 8
+               : M > 8192 ? 12
                : K < 2048 ? (M <= 1024 ? 21 : M < 4096 ? 14 : 7)
                : K == 2048 ? 17
                : K <= 4096 ? (M >= 4096 ? 28 : 23)
                            : (M < 2048 ? 30 : 47);
     case QMM_Q5_0:
-        return M > 8192   ? 12
+        return M > 24576  ? 8
+               : M > 8192 ? 12
                : K < 2048 ? (M <= 1024 ? 23 : M < 4096 ? 16 : 8)
                : K == 2048 ? 19
                : K <= 4096 ? (M >= 4096 ? 32 : 26)
                            : (M < 2048 ? 33 : 51);
     default:  // Q8_0
-        return M > 8192   ? 10
+        return M > 24576  ? 7
+               : M > 8192 ? 10
                : K < 2048 ? (M <= 1024 ? 26 : M < 4096 ? 15 : 7)
                : K == 2048 ? 17
                : K <= 4096 ? 26

@@ -146,8 +146,8 @@ int qmm_dequantize(int type, const void* blocks, float* out, int64_t rows, int64
  * N > 54 when M < 2048, else N > 30; for Q4_K N > 4 when
  * M > 8192 and K < 4096, else N > 2 (Q4_K with N <= 32
  * takes narrow MFMA kernels, on 32- or 16-row tiles, that split K over the
- * waves of a workgroup); for Q4_0 / Q5_0 / Q8_0, N > 12 / 12 / 10 when
- * M > 8192, else, when K < 2048, N > 21 / 23 / 26 for M <= 1024,
+ * waves of a workgroup); for Q4_0 / Q5_0 / Q8_0, N > 8 / 8 / 7 when
+ * M > 24576, N > 12 / 12 / 10 when 8192 < M <= 24576, else, when K < 2048, N > 21 / 23 / 26 for M <= 1024,
  * N > 14 / 16 / 15 for M < 4096 and N > 7 / 8 / 7 above; N > 17 / 19 / 17
  * when K = 2048; N > 28 / 32 / 26 when K <= 4096 and M >= 4096,
  * N > 23 / 26 / 26 when K <= 4096 and M < 4096; for wider rows

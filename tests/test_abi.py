@@ -148,11 +148,11 @@ def test_mul_mat_choice_cpu(L):
     assert [ch(Q.QMM_Q6_K, 8960, n, 1536) for n in (6, 7)] == [1, 2]
     assert [ch(Q.QMM_Q6_K, 1536, n, 8960) for n in (54, 55)] == [1, 2]
     # Q4_0 / Q5_0 / Q8_0: by rows above 8192, else by K and M
-    shapes = ((14336, 4096), (8960, 1536), (896, 896), (1536, 1536), (2048, 1024), (4864, 896),
+    shapes = ((32000, 4096), (65536, 2048), (14336, 4096), (8960, 1536), (896, 896), (1536, 1536), (2048, 1024), (4864, 896),
               (8192, 2048), (4096, 4096), (1024, 4096), (896, 4864), (1536, 8960), (2048, 8192))
-    for wt, t in ((Q.QMM_Q4_0, (12, 12, 21, 14, 14, 7, 17, 28, 23, 30, 30, 47)),
-                  (Q.QMM_Q5_0, (12, 12, 23, 16, 16, 8, 19, 32, 26, 33, 33, 51)),
-                  (Q.QMM_Q8_0, (10, 10, 26, 15, 15, 7, 17, 26, 26, 31, 31, 45))):
+    for wt, t in ((Q.QMM_Q4_0, (8, 8, 12, 12, 21, 14, 14, 7, 17, 28, 23, 30, 30, 47)),
+                  (Q.QMM_Q5_0, (8, 8, 12, 12, 23, 16, 16, 8, 19, 32, 26, 33, 33, 51)),
+                  (Q.QMM_Q8_0, (7, 7, 10, 10, 26, 15, 15, 7, 17, 26, 26, 31, 31, 45))):
         for (M, K), tm in zip(shapes, t):
             assert [ch(wt, M, n, K) for n in (tm, tm + 1)] == [1, 2], (wt, M, K)
         assert ch(wt, 8193, 40, 32768) == 2 and ch(wt, 4096, 33, 512) == 2
